@@ -1,0 +1,235 @@
+"""Benchmark of one DeepSeekMoE layer forward with bias-based balancing on one MI355X.
+
+A step is one pass of the whole path over one batch: route (router GEMM +
+sigmoid + biased group-limited top-k) -> dispatch (count, scan, permute) ->
+expert FFN (gate/up GEMM + SwiGLU, down GEMM; routed and shared) -> combine ->
+bias update.  Workload: the V3-like prefill layer in bf16 (T=16384 tokens,
+hidden 7168, 256 routed experts in 8 groups, at most 4 groups per token,
+top-8, 1 shared expert, intermediate 2048, gate scale 2.5), seeded synthetic
+inputs resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout (progress goes to stderr).  value = routed
+tokens/s of the whole layer.  The roofline object is for the dominant kernel,
+the gate/up grouped GEMM, timed live with HIP events on the stream it runs
+on.  cpu_baseline times the plain CPU oracle on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer (V3-like bf16); % MFMA peak; route GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_prefill_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def stage_bytes(c):
+    """Algorithmic HBM bytes of the bandwidth-bound stages (per layer pass)."""
+    a = 2  # bf16
+    route = c.T * c.E * 4 + c.E * 4 + c.T * c.k * 8                      # scores in, bias, idx + w out
+    router = c.T * c.H * a + c.E * c.H * a + c.T * c.E * 4                # x + W_r in, scores out
+    dispatch = c.T * c.H * a + c.T * c.k * c.H * a + c.T * c.k * 4 * 4   # x in, x_perm out, idx in, perm/inv out
+    combine = c.T * c.k * c.H * a + c.T * c.H * a * (2 if c.S else 1) + c.T * c.k * 8
+    return dict(router=router, topk=route, dispatch=dispatch, combine=combine)
+
+
+def cpu_baseline(c, x, w, bias, budget_s):
+    """Plain numpy oracle on a bounded sample; returns the layer rate it implies."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t_rows = min(c.T, 1024)
+    rows = slice(0, t_rows)
+    x32 = oracle.decode_act(x[rows]).astype(np.float64)
+    t0 = time.perf_counter()
+    s = oracle.affinity(x32, oracle.decode_act(w.w_router), w.logit_offset)
+    idx, gates = oracle.route(s, bias, c.G, c.M, c.k, c.group_topr, c.route_scale)
+    counts, offsets, perm, inv = oracle.dispatch(idx, c.E)
+    t_route = time.perf_counter() - t0
+    # expert FFN on whole segments of a few experts until the budget is used
+    t0 = time.perf_counter()
+    pairs_done = 0
+    order = np.argsort(-counts)
+    e_used = 0
+    for e in order:
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xp = oracle.decode_act(x[rows][perm[lo:hi] // c.k])
+        oracle.swiglu(xp, oracle.decode_act(w.w_gate_up[e]), oracle.decode_act(w.w_down[e]))
+        pairs_done += hi - lo
+        e_used += 1
+        if time.perf_counter() - t0 > budget_s * 0.6:
+            break
+    t_routed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    sh_rows = min(t_rows, 256)
+    ysh = oracle.shared_ffn(x32[:sh_rows], [oracle.decode_act(a) for a in w.ws_gate_up],
+                            [oracle.decode_act(a) for a in w.ws_down])
+    t_shared = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    yp = np.zeros((t_rows * c.k, c.H))
+    oracle.combine(yp, np.zeros((t_rows, c.H)), inv, gates)
+    t_combine = time.perf_counter() - t0
+    # extrapolate to the whole batch
+    per_token = (t_route + t_combine) / t_rows + t_routed / pairs_done * c.k + t_shared / sh_rows
+    layer_s = per_token * c.T
+    del ysh
+    return {"value": c.T / layer_s, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "host_cores": cores,
+            "sample": (f"{t_rows} of {c.T} tokens routed/dispatched/combined in fp64 numpy; expert FFN on "
+                       f"{pairs_done} (token,expert) pairs over {e_used} whole expert segments; shared expert "
+                       f"on {sh_rows} tokens; rate extrapolated per token to T={c.T}"),
+            "measured_s": round(t_route + t_routed + t_shared + t_combine, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the layer library has no multi-GPU path; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    from biased_top_routing_amd.runner import MoeLayerGPU, to_device
+    from workloads import CONFIGS
+    from workloads.inputs import make_weights, make_x
+
+    L.lib()     # fails loudly without the built library
+    c = CONFIGS[args.workload]
+    assert c.wgt == "bf16", "the headline bench is the bf16 workload"
+    torch.cuda.set_device(0)
+    log(f"workload {c.name}: generating seeded inputs")
+    t0 = time.perf_counter()
+    w = make_weights(c)
+    xh = make_x(c, 0)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
+    layer = MoeLayerGPU(c, w)
+    x = to_device(xh)
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    torch.cuda.synchronize()
+    log("uploaded; warming up")
+
+    names = ["route", "dispatch", "gate_up", "down", "combine", "bias"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        layer.route(x, bias)
+        if ev is not None:
+            ev[1].record()
+        layer.dispatch(x)
+        if ev is not None:
+            ev[2].record()
+        layer.expert_ffn(x, L.MOE_FFN_GATE_UP)
+        if ev is not None:
+            ev[3].record()
+        layer.expert_ffn(x, L.MOE_FFN_DOWN)
+        if ev is not None:
+            ev[4].record()
+        layer.combine()
+        if ev is not None:
+            ev[5].record()
+        layer.update_bias(bias, c.gamma)
+        if ev is not None:
+            ev[6].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    value = c.T / (wall / args.steps)
+    counts = layer.counts.cpu().numpy()
+    log(f"{ms_per_step:.3f} ms/step, {value:,.0f} tokens/s; stages {stage_ms}")
+
+    gu_flops = c.gate_up_flops()
+    dn_flops = c.down_flops()
+    gu_tflops = gu_flops / (stage_ms["gate_up"] * 1e-3) / 1e12
+    dn_tflops = dn_flops / (stage_ms["down"] * 1e-3) / 1e12
+    total_flops = gu_flops + dn_flops + c.router_flops()
+    b = stage_bytes(c)
+    route_gbs = (b["router"] + b["topk"]) / (stage_ms["route"] * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "T": c.T, "H": c.H, "E": c.E, "G": c.G, "M": c.M, "k": c.k, "S": c.S,
+                   "I": c.I, "route_scale": c.route_scale, "parallelism": "single-gpu"},
+        "roofline": {
+            "kernel": "gemm_bf16_kernel<gate_up> (routed + shared gate/up GEMM with fused SwiGLU)",
+            "bound": "mfma",
+            "achieved": round(gu_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": gu_flops,
+            "avg_launch_ms": round(stage_ms["gate_up"], 4),
+        },
+        "stages": {
+            "ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "down_tflops": round(dn_tflops, 2),
+            "layer_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
+            "route_gbs": round(route_gbs, 1),
+            "dispatch_gbs": round(b["dispatch"] / (stage_ms["dispatch"] * 1e-3) / 1e9, 1),
+            "combine_gbs": round(b["combine"] / (stage_ms["combine"] * 1e-3) / 1e9, 1),
+            "hbm_peak_gbs": PEAK_HBM_GBS,
+            "max_over_mean_load": round(float(counts.max() / (c.T * c.k / c.E)), 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(c, xh, w, w.bias0, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

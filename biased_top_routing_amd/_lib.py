@@ -1,0 +1,183 @@
+"""ctypes binding of libmoe.so: the five layer calls plus helpers, same names as the C ABI.
+
+Argument marshalling only.  Tensor arguments are torch tensors on the GPU (or
+raw integer device addresses, or None for NULL); the stream defaults to torch's
+current stream.  Every call raises MoeError on a non-zero status.  There is no
+fallback: if libmoe.so is missing the import of the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_SCORES_IN = 1
+MOE_FFN_ALL, MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1, 2
+MOE_WS_DISPATCH, MOE_WS_FFN = 1, 2
+_DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "E", "G", "M", "k", "S", "I", "group_topr")] + [
+        ("route_scale", ctypes.c_float), ("act", ctypes.c_int32), ("wgt", ctypes.c_int32),
+        ("bias_eq_mode", ctypes.c_int32)]
+
+
+class MoeExpertWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "w_gate_up", "w_down", "w_gate_up_scale", "w_down_scale",
+        "ws_gate_up", "ws_down", "ws_gate_up_scale", "ws_down_scale")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built by biased_top_routing_amd.build); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run python -m biased_top_routing_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, u32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+        cfgp = ctypes.POINTER(MoeCfg)
+        sig = {
+            "moe_route": [cfgp, vp, vp, vp, vp, vp, u32, vp, vp, vp],
+            "moe_dispatch": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_expert_ffn": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp, sz,
+                               ctypes.c_int, vp],
+            "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp],
+            "moe_update_bias": [cfgp, vp, vp, f32, vp],
+            "moe_quantize_fp8": [vp, i32, i32, i32, i32, vp, vp, vp],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.moe_workspace_bytes.argtypes = [cfgp, ctypes.c_int]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_abi_version.argtypes = []
+        L.moe_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/moe.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|size_t|const char\*|int)\s+(moe_\w+)\s*\(", text, re.M)))
+
+
+def make_cfg(T, H, E, G, M, k, S, I, group_topr=2, route_scale=1.0, act="bf16", wgt="bf16",
+             bias_eq_mode=0) -> MoeCfg:
+    a = _DTYPES[act] if isinstance(act, str) else act
+    w = _DTYPES[wgt] if isinstance(wgt, str) else wgt
+    return MoeCfg(T, H, E, G, M, k, S, I, group_topr, route_scale, a, w, bias_eq_mode)
+
+
+def cfg_from(c, **over) -> MoeCfg:
+    """MoeCfg from any object with the layer attributes (T H E G M k S I group_topr
+    route_scale act wgt bias_eq_mode)."""
+    d = {n: getattr(c, n) for n in ("T", "H", "E", "G", "M", "k", "S", "I", "group_topr", "route_scale",
+                                     "act", "wgt")}
+    d["bias_eq_mode"] = getattr(c, "bias_eq_mode", 0)
+    d.update(over)
+    return make_cfg(**d)
+
+
+def _p(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _s(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _check(name: str, st: int) -> None:
+    if st != MOE_OK:
+        raise MoeError(name, st)
+
+
+def moe_route(cfg, x, w_router, logit_offset, bias, scores, flags, topk_idx, topk_w, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(bias),
+                                        _p(scores), flags, _p(topk_idx), _p(topk_w), _s(stream)))
+
+
+def moe_dispatch(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale, ws, stream=None):
+    _check("moe_dispatch", lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts), _p(offsets),
+                                              _p(perm), _p(inv), _p(x_perm), _p(x_perm_scale), _p(ws),
+                                              _nbytes(ws), _s(stream)))
+
+
+def expert_weights(w_gate_up, w_down, ws_gate_up=None, ws_down=None, w_gate_up_scale=None,
+                   w_down_scale=None, ws_gate_up_scale=None, ws_down_scale=None) -> MoeExpertWeights:
+    return MoeExpertWeights(_p(w_gate_up), _p(w_down), _p(w_gate_up_scale), _p(w_down_scale),
+                            _p(ws_gate_up), _p(ws_down), _p(ws_gate_up_scale), _p(ws_down_scale))
+
+
+def moe_expert_ffn(cfg, x_perm, x_perm_scale, offsets, weights: MoeExpertWeights, x, y_perm, y_shared, ws,
+                   phase=MOE_FFN_ALL, stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(x_perm_scale), _p(offsets),
+                                                  ctypes.byref(weights), _p(x), _p(y_perm), _p(y_shared),
+                                                  _p(ws), _nbytes(ws), phase, _s(stream)))
+
+
+def moe_combine(cfg, y_perm, y_shared, inv, topk_w, y, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _p(y_perm), _p(y_shared), _p(inv), _p(topk_w),
+                                            _p(y), _s(stream)))
+
+
+def moe_update_bias(cfg, counts, bias, gamma, stream=None):
+    _check("moe_update_bias", lib().moe_update_bias(ctypes.byref(cfg), _p(counts), _p(bias), float(gamma),
+                                                    _s(stream)))
+
+
+def moe_quantize_fp8(src, n_mat, rows, cols, block_rows, dst, scales, stream=None):
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(src), n_mat, rows, cols, block_rows, _p(dst),
+                                                      _p(scales), _s(stream)))
+
+
+def moe_workspace_bytes(cfg, which) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(cfg), which))
+
+
+def status_string(st: int) -> str:
+    try:
+        return lib().moe_status_string(st).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+moe_status_string = status_string
+
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())

@@ -1,0 +1,117 @@
+// moe_combine: gated gather of the routed expert outputs plus the shared output.
+// moe_update_bias: the per-step +-gamma balancing rule.
+//
+// Combine weights each routed output by its gate, which comes from the raw
+// affinity (DeepSeek-V3 Technical Report：中英对照解读, §2.2 and §3).  The bias
+// update follows the reading notes (Method §1 "Auxiliary-loss-free 负载均衡")
+// and the qwbw.cn essay's load-balancing section: after each step an
+// overloaded expert's bias falls by gamma and an underloaded one's rises.
+#include "common.h"
+
+namespace moe {
+
+// One wavefront per token; 16-byte chunks (8 bf16 or 4 fp32 values) per lane.
+// y = y_shared + sum_j w_j * y_perm[inv_j], fp32 accumulation, j ascending.
+template <bool BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y_perm,
+                                                      const uint4* __restrict__ y_shared,
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int k, int64_t nchunk,
+                                                      uint4* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t myp = lane < k ? inv[t * k + lane] : 0;
+  const float myw = lane < k ? topk_w[t * k + lane] : 0.f;
+  constexpr int V = BF16 ? 8 : 4;
+  for (int64_t c = lane; c < nchunk; c += kWave) {
+    float acc[V];
+    if (y_shared) {
+      const uint4 r = y_shared[t * nchunk + c];
+      const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+          acc[2 * i] = bf16_to_f32((bf16_t)(w4[i] & 0xFFFF));
+          acc[2 * i + 1] = bf16_to_f32((bf16_t)(w4[i] >> 16));
+        } else {
+          acc[i] = __uint_as_float(w4[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    }
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = __shfl(myp, j);
+      const float g = __shfl(myw, j);
+      const uint4 r = y_perm[p * nchunk + c];
+      const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (BF16) {
+          acc[2 * i] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] & 0xFFFF)), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] >> 16)), acc[2 * i + 1]);
+        } else {
+          acc[i] = fmaf(g, __uint_as_float(w4[i]), acc[i]);
+        }
+      }
+    }
+    uint4 o;
+    if (BF16) {
+      o = make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                     pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7]));
+    } else {
+      o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                     __float_as_uint(acc[3]));
+    }
+    y[t * nchunk + c] = o;
+  }
+}
+
+// One thread per expert; fp32 adds with round-to-nearest-even.
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts,
+                                                          float* __restrict__ bias, int E,
+                                                          int64_t total, float gamma, int eq_mode) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const int64_t load = (int64_t)counts[e] * E;
+  const float b = bias[e];
+  if (load > total) bias[e] = b - gamma;
+  else if (load < total || eq_mode == 0) bias[e] = b + gamma;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_combine(const moe_cfg* cfg, const void* y_perm, const void* y_shared,
+                                  const int32_t* inv, const float* topk_w, void* y, void* stream) {
+  moe_status st = validate_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!y_perm || !inv || !topk_w || !y) return MOE_ERR_NULL;
+  if (cfg->S > 0 && !y_shared) return MOE_ERR_NULL;
+  if (cfg->T == 0) return MOE_OK;
+  const int64_t nchunk = (int64_t)cfg->H * act_bytes(cfg) / 16;
+  const dim3 grid((unsigned)((cfg->T + 3) / 4));
+  const uint4* ysh = cfg->S > 0 ? (const uint4*)y_shared : nullptr;
+  if (cfg->act == MOE_F32)
+    hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, as_stream(stream), (const uint4*)y_perm,
+                       ysh, inv, topk_w, cfg->T, cfg->k, nchunk, (uint4*)y);
+  else
+    hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, as_stream(stream), (const uint4*)y_perm,
+                       ysh, inv, topk_w, cfg->T, cfg->k, nchunk, (uint4*)y);
+  return launch_status();
+}
+
+extern "C" moe_status moe_update_bias(const moe_cfg* cfg, const int32_t* counts, float* bias, float gamma,
+                                      void* stream) {
+  moe_status st = validate_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!counts || !bias) return MOE_ERR_NULL;
+  if (!(gamma == gamma)) return MOE_ERR_SHAPE;
+  hipLaunchKernelGGL(bias_update_kernel, dim3((cfg->E + 255) / 256), dim3(256), 0, as_stream(stream), counts,
+                     bias, cfg->E, pairs(cfg), gamma, cfg->bias_eq_mode);
+  return launch_status();
+}

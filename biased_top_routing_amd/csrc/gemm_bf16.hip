@@ -1,0 +1,297 @@
+// bf16 MFMA GEMMs of the layer on gfx950 (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
+//   router   scores[T,E] = sigmoid(x W_r^T + o)
+//   gate/up  h = silu(X W_g^T) * (X W_u^T) per expert segment (routed) and over all
+//            tokens for the shared experts; h stored as bf16
+//   down     Y = h W_d^T per segment; Y stored as bf16
+// The layer's experts are SwiGLU FFNs of shared and routed experts (DeepSeek-V3
+// Technical Report：中英对照解读, §2 Architecture); the router stays in bf16
+// with fp32 accumulation (qwbw.cn essay, FP8 part of the infrastructure section,
+// keeps MoE gating in BF16/FP32).
+//
+// Tiling: a 256-thread workgroup computes a (2*MI*32) x 256 tile with four
+// wavefronts in a 2 x 2 grid; each wavefront owns MI x 4 MFMA 32x32 blocks.  A
+// and B K-slices of BK columns are staged through LDS (double-buffered, one
+// barrier per K step) with an XOR swizzle of the 16-byte chunks so that the
+// MFMA operand reads (32 rows x 16 bytes per half wave) hit distinct banks.
+// For gate/up, the tile's 256 weight rows are 128 gate rows and the 128 up rows
+// of the same intermediate columns, so SwiGLU is applied in registers.
+// Grouped tiles come from a device-built table (segment, first row, rows,
+// column tile) ordered column-tile-major inside a segment; the table is cut
+// into 8 contiguous ranges, one per XCD (workgroup id mod 8), so tiles sharing
+// a weight panel run together in one XCD's L2.
+#include "common.h"
+#include "ffn_layout.h"
+#include "kernels.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+enum { kRouter = 0, kGateUp = 1, kDown = 2 };
+
+struct GemmParams {
+  const bf16_t* a_routed;   // gate/up: x_perm [P,H]; down: h_perm [P,I]
+  const bf16_t* a_shared;   // gate/up and router: x [T,H]; down: h_shared [T,S*I]
+  const bf16_t* w_routed;   // gate/up: w_gate_up; down: w_down; router: w_router
+  const bf16_t* w_shared;   // gate/up: ws_gate_up; down: ws_down
+  const float* offset;      // router logit offset (nullable)
+  void* out_routed;         // gate/up: h_perm; down: y_perm; router: scores (fp32)
+  void* out_shared;         // gate/up: h_shared; down: y_shared
+  const TileDesc* tiles;
+  const int32_t* ntiles;
+  int T, H, E, S, I;
+};
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per row).
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CPR == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  else return c ^ (((r >> 1) ^ (r >> 2)) & 3);   // CPR == 4
+}
+
+template <int MODE, int MI, int BK>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int BM = 2 * MI * 32;
+  constexpr int BN = 256;
+  constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
+  constexpr int A_CH = BM * CPR / 256;    // A chunks loaded per thread per K step
+  constexpr int B_CH = BN * CPR / 256;
+  constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
+  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ------------------------------------------------------------ which tile
+  int seg = 0, row0, rows, nt;
+  if constexpr (MODE == kRouter) {
+    row0 = blockIdx.x * BM;
+    rows = min(BM, p.T - row0);
+    nt = blockIdx.y;
+  } else {
+    const int n_real = *p.ntiles;
+    const int per = (n_real + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    if (j >= per) return;
+    const int L = xcd * per + j;
+    if (L >= n_real) return;
+    const TileDesc d = p.tiles[L];
+    seg = d.seg; row0 = d.row0; rows = d.rows; nt = d.nt;
+  }
+  const bool shared = (MODE != kRouter) && seg == p.E;
+
+  // ------------------------------------------------------------ operand bases
+  const bf16_t* A;
+  int lda;
+  if constexpr (MODE == kDown) {
+    A = shared ? p.a_shared : p.a_routed;
+    lda = shared ? p.S * p.I : p.I;
+  } else {
+    A = (MODE == kRouter || shared) ? p.a_shared : p.a_routed;
+    lda = p.H;
+  }
+  const int K = lda;
+  A += (int64_t)row0 * lda;
+
+  const bf16_t* W;
+  int ldw;
+  int64_t seg_kstride = 0;   // down, shared: next shared expert's W_d every I columns of K
+  if constexpr (MODE == kRouter) {
+    W = p.w_routed;
+    ldw = p.H;
+  } else if constexpr (MODE == kGateUp) {
+    const int n0 = nt * kBNH;
+    const int sexp = n0 / p.I, c0 = n0 % p.I;
+    W = (shared ? p.w_shared : p.w_routed + (int64_t)seg * 2 * p.I * p.H) +
+        ((int64_t)sexp * 2 * p.I + c0) * p.H;
+    ldw = p.H;
+  } else {
+    W = shared ? p.w_shared : p.w_routed + (int64_t)seg * p.H * p.I;
+    ldw = p.I;
+    seg_kstride = (int64_t)p.H * p.I;
+  }
+
+  int a_off[A_CH], a_lds[A_CH], b_off[B_CH], b_lds[B_CH];
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+    a_off[i] = min(r, rows - 1) * lda + c * 8;
+    a_lds[i] = r * BK + swz<CPR>(r, c) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) {
+    const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+    int wrow;
+    if constexpr (MODE == kRouter) wrow = min(nt * BN + r, p.E - 1);
+    else if constexpr (MODE == kGateUp) wrow = r < 128 ? r : p.I + (r - 128);
+    else wrow = min(nt * BN + r, p.H - 1);
+    b_off[i] = wrow * ldw + c * 8;
+    b_lds[i] = BM * BK + r * BK + swz<CPR>(r, c) * 8;
+  }
+
+  uint4 ra[A_CH], rb[B_CH];
+#define MOE_GLOAD(k0_)                                                                        \
+  {                                                                                           \
+    const int k0v = (k0_);                                                                    \
+    const bf16_t* Wk = W + (MODE == kDown ? (int64_t)(k0v / p.I) * seg_kstride + (k0v % p.I)  \
+                                          : (int64_t)k0v);                                    \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                          \
+        ra[i] = *reinterpret_cast<const uint4*>(A + a_off[i] + k0v);                          \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                          \
+        rb[i] = *reinterpret_cast<const uint4*>(Wk + b_off[i]);                               \
+  }
+#define MOE_LSTORE(buf_)                                                                      \
+  {                                                                                           \
+    bf16_t* sbase = lds + (buf_) * STAGE;                                                     \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                          \
+        *reinterpret_cast<uint4*>(sbase + a_lds[i]) = ra[i];                                  \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                          \
+        *reinterpret_cast<uint4*>(sbase + b_lds[i]) = rb[i];                                  \
+  }
+
+  f32x16_t acc[MI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+
+  int a_rd[MI], b_rd[4];
+  const int lr = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) a_rd[mi] = wm * MI * 32 + mi * 32 + lr;
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int brow = (MODE == kGateUp) ? (ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 : wn * 128 + ni * 32;
+    b_rd[ni] = brow + lr;
+  }
+
+  const int nk = K / BK;
+  MOE_GLOAD(0);
+  MOE_LSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    MOE_GLOAD((kt + 1 < nk ? kt + 1 : kt) * BK);   // the last step reloads its own slice
+    const bf16_t* base = lds + cur * STAGE;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int c = kk * 2 + kh;
+      bf16x8_t a[MI], b[4];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        a[mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + swz<CPR>(a_rd[mi], c) * 8);
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        b[ni] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + b_rd[ni] * BK +
+                                                   swz<CPR>(b_rd[ni], c) * 8);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (kt + 1 < nk) MOE_LSTORE(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ------------------------------------------------------------ epilogue
+  // acc[mi][ni][r] holds C[i][j] with j = lane % 32 and
+  // i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 inside the 32 x 32 block.
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (i >= rows) continue;
+      const int64_t row = row0 + i;
+      if constexpr (MODE == kGateUp) {
+        const int ldo = shared ? p.S * p.I : p.I;
+        bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const float g = acc[mi][ni][r], u = acc[mi][ni + 2][r];
+          const float h = g / (1.0f + __expf(-g)) * u;
+          out[row * ldo + nt * kBNH + wn * 64 + ni * 32 + lr] = f32_to_bf16(h);
+        }
+      } else if constexpr (MODE == kDown) {
+        bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = nt * BN + wn * 128 + ni * 32 + lr;
+          if (col < p.H) out[row * p.H + col] = f32_to_bf16(acc[mi][ni][r]);
+        }
+      } else {
+        float* out = static_cast<float*>(p.out_routed);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = nt * BN + wn * 128 + ni * 32 + lr;
+          if (col < p.E) {
+            const float l = acc[mi][ni][r] + (p.offset ? p.offset[col] : 0.f);
+            out[row * p.E + col] = 1.0f / (1.0f + expf(-l));
+          }
+        }
+      }
+    }
+  }
+#undef MOE_GLOAD
+#undef MOE_LSTORE
+}
+
+moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
+                              const float* offset, float* scores, hipStream_t st) {
+  GemmParams p{};
+  p.a_shared = x;
+  p.w_routed = w_router;
+  p.offset = offset;
+  p.out_routed = scores;
+  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
+  const dim3 grid((unsigned)((c->T + 63) / 64), (unsigned)((c->E + 255) / 256));
+  hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, 1, 64>), grid, dim3(256), 0, st, p);
+  return launch_status();
+}
+
+moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t* offsets,
+                           const moe_expert_weights* w, const bf16_t* x, bf16_t* y_perm,
+                           bf16_t* y_shared, void* ws, int phase, hipStream_t st) {
+  const FfnLayout L(c);
+  char* base = static_cast<char*>(ws);
+  const int32_t* hdr = reinterpret_cast<const int32_t*>(base + L.off_hdr);
+  bf16_t* hp = reinterpret_cast<bf16_t*>(base + L.off_hp);
+  bf16_t* hs = reinterpret_cast<bf16_t*>(base + L.off_hs);
+  moe_status s;
+  if (phase == MOE_FFN_ALL || phase == MOE_FFN_GATE_UP) {
+    if ((s = launch_build_tiles(c, offsets, ws, st)) != MOE_OK) return s;
+    GemmParams p{};
+    p.a_routed = x_perm; p.a_shared = x;
+    p.w_routed = (const bf16_t*)w->w_gate_up; p.w_shared = (const bf16_t*)w->ws_gate_up;
+    p.out_routed = hp; p.out_shared = hs;
+    p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t1);
+    p.ntiles = hdr;
+    p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
+    const int64_t grid = align_up((size_t)L.max1, 8);
+    if (grid > 0) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, 2, 64>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      if ((s = launch_status()) != MOE_OK) return s;
+    }
+  }
+  if (phase == MOE_FFN_ALL || phase == MOE_FFN_DOWN) {
+    GemmParams p{};
+    p.a_routed = hp; p.a_shared = hs;
+    p.w_routed = (const bf16_t*)w->w_down; p.w_shared = (const bf16_t*)w->ws_down;
+    p.out_routed = y_perm; p.out_shared = y_shared;
+    p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t2);
+    p.ntiles = hdr + 1;
+    p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
+    const int64_t grid = align_up((size_t)L.max2, 8);
+    if (grid > 0) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, 2, 64>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      if ((s = launch_status()) != MOE_OK) return s;
+    }
+  }
+  return MOE_OK;
+}
+
+}  // namespace moe

@@ -1,0 +1,114 @@
+"""Device buffers for one MoE layer and the five C-ABI calls in order.
+
+MoeLayerGPU uploads a layer's weights once, allocates every buffer the calls
+need for T tokens, and runs route -> dispatch -> expert FFN -> combine ->
+bias update on the current stream.  It only allocates and marshals; every step
+of the layer runs in libmoe's kernels.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def to_device(arr, device="cuda"):
+    """numpy float32 -> float32 tensor; numpy uint16 (bf16 bit patterns) -> bfloat16 tensor."""
+    if arr is None:
+        return None
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(arr).to(device)
+
+
+class MoeLayerGPU:
+    def __init__(self, cfg, weights, T=None, device="cuda"):
+        self.c = cfg
+        self.device = device
+        self.fp8 = cfg.wgt == "fp8_e4m3"
+        self.act_dtype = torch.float32 if cfg.act == "f32" else torch.bfloat16
+        dev = lambda a: to_device(a, device)
+        self.w_router = dev(weights.w_router)
+        self.logit_offset = dev(weights.logit_offset)
+        if self.fp8:
+            self.w_gate_up, self.w_gate_up_scale = self._quantize(weights.w_gate_up)
+            self.w_down, self.w_down_scale = self._quantize(weights.w_down)
+            self.ws_gate_up, self.ws_gate_up_scale = self._quantize(weights.ws_gate_up)
+            self.ws_down, self.ws_down_scale = self._quantize(weights.ws_down)
+        else:
+            self.w_gate_up, self.w_down = dev(weights.w_gate_up), dev(weights.w_down)
+            self.ws_gate_up, self.ws_down = dev(weights.ws_gate_up), dev(weights.ws_down)
+            self.w_gate_up_scale = self.w_down_scale = self.ws_gate_up_scale = self.ws_down_scale = None
+        self.weights = L.expert_weights(self.w_gate_up, self.w_down, self.ws_gate_up, self.ws_down,
+                                        self.w_gate_up_scale, self.w_down_scale, self.ws_gate_up_scale,
+                                        self.ws_down_scale)
+        self.alloc(cfg.T if T is None else T)
+
+    def _quantize(self, w_np):
+        """bf16 weights [n, rows, cols] -> E4M3 codes + one fp32 scale per 128 x 128 block (on the GPU)."""
+        n, rows, cols = w_np.shape
+        codes = torch.empty((n, rows, cols), dtype=torch.uint8, device=self.device)
+        scales = torch.empty((n, rows // 128, cols // 128), dtype=torch.float32, device=self.device)
+        if n:
+            src = to_device(w_np, self.device)
+            L.moe_quantize_fp8(src, n, rows, cols, 128, codes, scales)
+            torch.cuda.current_stream().synchronize()
+            del src
+        return codes, scales
+
+    def alloc(self, T):
+        c = self.c
+        self.T = T
+        self.cfg = L.cfg_from(c, T=T)
+        d, P = self.device, T * c.k
+        f32, i32 = torch.float32, torch.int32
+        self.scores = torch.empty((T, c.E), dtype=f32, device=d)
+        self.topk_idx = torch.empty((T, c.k), dtype=i32, device=d)
+        self.topk_w = torch.empty((T, c.k), dtype=f32, device=d)
+        self.counts = torch.empty(c.E, dtype=i32, device=d)
+        self.offsets = torch.empty(c.E + 1, dtype=i32, device=d)
+        self.perm = torch.empty(P, dtype=i32, device=d)
+        self.inv = torch.empty((T, c.k), dtype=i32, device=d)
+        if self.fp8:
+            self.x_perm = torch.empty((P, c.H), dtype=torch.uint8, device=d)
+            self.x_perm_scale = torch.empty((P, c.H // 128), dtype=f32, device=d)
+        else:
+            self.x_perm = torch.empty((P, c.H), dtype=self.act_dtype, device=d)
+            self.x_perm_scale = None
+        self.y_perm = torch.empty((P, c.H), dtype=self.act_dtype, device=d)
+        self.y_shared = torch.empty((T, c.H), dtype=self.act_dtype, device=d) if c.S > 0 else None
+        self.y = torch.empty((T, c.H), dtype=self.act_dtype, device=d)
+        self.ws_dispatch = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_DISPATCH), dtype=torch.uint8,
+                                       device=d)
+        self.ws_ffn = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_FFN), dtype=torch.uint8, device=d)
+
+    # ---------------------------------------------------------------- the five calls
+    def route(self, x, bias, scores_in=False):
+        L.moe_route(self.cfg, x, self.w_router, self.logit_offset, bias, self.scores,
+                    L.MOE_SCORES_IN if scores_in else 0, self.topk_idx, self.topk_w)
+
+    def dispatch(self, x):
+        L.moe_dispatch(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv, self.x_perm,
+                       self.x_perm_scale, self.ws_dispatch)
+
+    def expert_ffn(self, x, phase=L.MOE_FFN_ALL):
+        L.moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_scale, self.offsets, self.weights, x, self.y_perm,
+                         self.y_shared, self.ws_ffn, phase)
+
+    def combine(self):
+        L.moe_combine(self.cfg, self.y_perm, self.y_shared, self.inv, self.topk_w, self.y)
+
+    def update_bias(self, bias, gamma):
+        L.moe_update_bias(self.cfg, self.counts, bias, gamma)
+
+    def forward(self, x, bias, gamma=None, scores_in=False):
+        """One batch through the layer; with gamma set, bias is updated in place afterwards."""
+        self.route(x, bias, scores_in)
+        self.dispatch(x)
+        self.expert_ffn(x)
+        self.combine()
+        if gamma is not None:
+            self.update_bias(bias, gamma)
+        return self.y

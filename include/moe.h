@@ -1,0 +1,229 @@
+/*
+ * moe.h - C ABI of a single-GPU DeepSeekMoE layer forward with auxiliary-loss-free
+ * (bias-based) load balancing, for AMD Instinct MI355X (gfx950).
+ *
+ * One batch runs as five calls on one HIP stream:
+ *   moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine -> moe_update_bias
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor argument is a DEVICE pointer owned by the caller; `cfg` and
+ *    `w` are HOST pointers read during the call only.  The library never
+ *    allocates or frees memory on these paths and keeps no state between calls.
+ *  - Tensors are dense, row-major, contiguous.  Weights are [out, in] (K is the
+ *    contiguous dimension of both GEMM operands).  Indices are int32.
+ *  - bf16 tensors are raw 16-bit bfloat16 values; fp8 tensors are raw OCP E4M3FN
+ *    bytes (bias 7, no infinities, largest finite 448).
+ *  - Every call validates all sizes and pointers on the host BEFORE touching the
+ *    device and returns a negative moe_status on error (nothing is launched).  A
+ *    failed launch returns MOE_ERR_LAUNCH.  Work is asynchronous on `stream`
+ *    (a hipStream_t; NULL means the default stream); device faults surface at
+ *    the caller's next synchronisation.  The library never synchronises.
+ *  - Calls are re-entrant; calls on one stream are ordered by that stream.
+ *    Two calls that share an output or workspace buffer on different streams
+ *    race.
+ *
+ * Results: expert indices, counts, the permutation and the bias update are
+ * deterministic bit for bit (no atomics anywhere on the path).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* sizes inconsistent or outside the supported range */
+  MOE_ERR_UNSUPPORTED = -3, /* dtype combination or option not implemented */
+  MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_LAUNCH = -5       /* a kernel launch failed (hipGetLastError) */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/*
+ * Layer configuration.
+ *  T tokens, H hidden, E routed experts in G contiguous groups of E/G experts,
+ *  at most M groups per token, k routed experts per token, S shared experts,
+ *  I intermediate size of each expert.
+ *  group_topr: a group's score is the fp32 sum of its group_topr largest biased
+ *              scores, added from the largest down (1 <= group_topr <= E/G, <= 8).
+ *  route_scale: gates are route_scale * s_j / sum(s) over the selected experts.
+ *  act / wgt (moe_dtype): (F32, F32) | (BF16, BF16) | (BF16, FP8_E4M3).  The
+ *              router always runs in `act` precision; FP8_E4M3 applies to the
+ *              expert GEMMs only.
+ *  bias_eq_mode: 0 - an expert whose load equals T*k/E counts as underloaded
+ *              (+gamma), so every bias moves each step; 1 - it is left unchanged.
+ * Supported ranges: 1 <= G <= 64, E % G == 0, E <= 512, 1 <= M <= G,
+ *  1 <= k <= min(32, M*E/G), T >= 0, T*k < 2^31, H % 8 == 0 and I % 8 == 0
+ *  (F32: H % 4 == 0, I % 4 == 0); BF16 expert GEMMs need H % 64 == 0 and
+ *  I % 128 == 0; FP8 needs H % 128 == 0 and I % 128 == 0.
+ */
+typedef struct {
+  int32_t T, H, E, G, M, k, S, I;
+  int32_t group_topr;
+  float route_scale;
+  int32_t act;
+  int32_t wgt;
+  int32_t bias_eq_mode;
+} moe_cfg;
+
+/* moe_route flags */
+#define MOE_SCORES_IN 1u /* `scores` is an input: route on these fp32 affinities, skip the router GEMM */
+
+/*
+ * moe_route - affinity and biased, group-limited top-k with gates.
+ *
+ * Follows: each expert's bias enters only the ranking used for top-K selection
+ * while the gating value comes from the original affinity (DeepSeek-V3
+ * Technical Report reading notes, Method §1 "Auxiliary-loss-free 负载均衡";
+ * DeepSeek-V3 Technical Report：中英对照解读, §3; DeepSeek V3 product page,
+ * "公式解密" box: ranking score = affinity + bias); a token goes to at most M
+ * nodes (reading notes, Method §1), here M of G expert groups.
+ *
+ *  x            [T, H] act dtype                 (unused with MOE_SCORES_IN)
+ *  w_router     [E, H] act dtype                 (unused with MOE_SCORES_IN)
+ *  logit_offset [E] fp32 added to the logits before the sigmoid, or NULL
+ *  bias         [E] fp32 routing bias b
+ *  scores       [T, E] fp32: output s = sigmoid(x w_router^T + o), or the input
+ *               affinities with MOE_SCORES_IN
+ *  topk_idx     [T, k] int32 out: selected experts, ordered by s + b descending,
+ *               ties to the lower expert index (-0.0 ranks as +0.0)
+ *  topk_w       [T, k] fp32 out: route_scale * s_j / sum_j s_j
+ * Groups are chosen first (the M largest group scores, ties to the lower group),
+ * then the k largest s + b among the experts of the chosen groups.
+ * NaN scores give unspecified indices.
+ */
+moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
+                     const float* logit_offset, const float* bias, float* scores,
+                     uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * moe_dispatch - per-expert loads and the expert-sorted permutation of the
+ * (token, slot) pairs, plus the permuted activations.
+ *
+ * Follows: tokens are dispatched to their experts and combined back
+ * (DeepSeek-V3 Technical Report：中英对照解读, §2.2); each expert's load is
+ * counted over the whole batch (qwbw.cn essay on the DeepSeek-V3 report,
+ * load-balancing section).
+ *
+ *  topk_idx  [T, k] int32 in (values in [0, E); out-of-range values are undefined)
+ *  x         [T, H] act dtype in
+ *  counts    [E] int32 out: pairs routed to each expert
+ *  offsets   [E+1] int32 out: exclusive prefix sum of counts
+ *  perm      [T*k] int32 out: flat pair ids f = t*k + j, stably sorted by expert
+ *  inv       [T, k] int32 out: row of pair (t, j) in the permuted order
+ *  x_perm    [T*k, H] out: row p = x[perm[p] / k]; act dtype, or E4M3 bytes when
+ *            wgt == FP8_E4M3 (quantised per 1x128 tile: sc = amax/448, q = e4m3(v/sc))
+ *  x_perm_scale [T*k, H/128] fp32 out (FP8 only, else NULL)
+ *  ws, ws_bytes  workspace of at least moe_workspace_bytes(cfg, MOE_WS_DISPATCH)
+ */
+moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                        void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* Expert weights.  Scales are only read when wgt == FP8_E4M3 (then the weight
+ * tensors hold E4M3 bytes, one fp32 scale per 128 x 128 block). */
+typedef struct {
+  const void* w_gate_up;         /* [E, 2I, H]: gate rows [0, I), up rows [I, 2I) */
+  const void* w_down;            /* [E, H, I] */
+  const float* w_gate_up_scale;  /* [E, 2I/128, H/128] */
+  const float* w_down_scale;     /* [E, H/128, I/128] */
+  const void* ws_gate_up;        /* [S, 2I, H] shared experts */
+  const void* ws_down;           /* [S, H, I] */
+  const float* ws_gate_up_scale; /* [S, 2I/128, H/128] */
+  const float* ws_down_scale;    /* [S, H/128, I/128] */
+} moe_expert_weights;
+
+/* moe_expert_ffn phases: the two GEMM launches may be issued by separate calls
+ * (GATE_UP then DOWN, same workspace), e.g. to time them apart. */
+#define MOE_FFN_ALL 0
+#define MOE_FFN_GATE_UP 1
+#define MOE_FFN_DOWN 2
+
+/*
+ * moe_expert_ffn - routed experts on their segments of x_perm and the shared
+ * experts on every token, each a SwiGLU FFN: FFN(v) = W_d (silu(W_g v) * W_u v).
+ *
+ * Follows: shared experts that every token passes through plus routed experts
+ * picked by top-k (DeepSeek-V3 Technical Report：中英对照解读, §2); FP8 with
+ * 1x128 activation tiles and 128x128 weight blocks, E4M3 everywhere and
+ * full-precision accumulation (qwbw.cn essay, FP8 part of the infrastructure
+ * section; same notes, §6).
+ *
+ *  x_perm, x_perm_scale, offsets  as written by moe_dispatch
+ *  w            host pointer to the weight table
+ *  x            [T, H] act dtype (input of the shared experts)
+ *  y_perm       [T*k, H] out, act dtype: routed expert outputs, ungated
+ *  y_shared     [T, H] out, act dtype: sum of the shared experts' outputs (S > 0)
+ *  ws, ws_bytes at least moe_workspace_bytes(cfg, MOE_WS_FFN); holds the
+ *               SwiGLU intermediates between the two phases
+ *  phase        MOE_FFN_ALL | MOE_FFN_GATE_UP | MOE_FFN_DOWN
+ * Intermediates are rounded to the activation dtype (bf16) or, for FP8, to E4M3
+ * per 1x128 tile of each row; accumulation is fp32.
+ */
+moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                          const int32_t* offsets, const moe_expert_weights* w, const void* x,
+                          void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
+                          void* stream);
+
+/*
+ * moe_combine - y[t] = y_shared[t] + sum_j topk_w[t, j] * y_perm[inv[t, j]]
+ * accumulated in fp32 over j ascending; y in the activation dtype.
+ * Follows: combine of the expert outputs weighted by gating values taken from
+ * the raw affinities (DeepSeek-V3 Technical Report：中英对照解读, §2.2 and §3).
+ * y_shared may be NULL when S == 0.  No residual is added.
+ */
+moe_status moe_combine(const moe_cfg* cfg, const void* y_perm, const void* y_shared,
+                       const int32_t* inv, const float* topk_w, void* y, void* stream);
+
+/*
+ * moe_update_bias - the per-step balancing rule: for each expert,
+ * bias -= gamma if counts*E > T*k (overloaded), bias += gamma if underloaded
+ * (counts*E < T*k, or == with bias_eq_mode 0), in fp32 with round-to-nearest-even.
+ * Follows: reading notes, Method §1 "Auxiliary-loss-free 负载均衡"; qwbw.cn
+ * essay, load-balancing section (loads counted over the whole batch after each
+ * step).  bias is updated in place; counts as written by moe_dispatch.
+ */
+moe_status moe_update_bias(const moe_cfg* cfg, const int32_t* counts, float* bias, float gamma,
+                           void* stream);
+
+/*
+ * moe_quantize_fp8 - offline weight preparation for the FP8 expert GEMMs:
+ * a bf16 matrix [n_mat, rows, cols] becomes E4M3 bytes [n_mat, rows, cols]
+ * and one fp32 scale per 128 x 128 block [n_mat, rows/128, cols/128]
+ * (sc = amax/448, or 1 for an all-zero block; q = e4m3(v/sc), nearest-even,
+ * saturating).  Follows the 128x128 weight blocks of the pages' FP8 recipe
+ * (qwbw.cn essay, FP8 part of the infrastructure section).  With block_rows = 1
+ * it quantises per 1 x 128 tile instead (scales [n_mat, rows, cols/128]).
+ * rows must be a multiple of block_rows (1 or 128), cols of 128.
+ */
+moe_status moe_quantize_fp8(const void* src_bf16, int32_t n_mat, int32_t rows, int32_t cols,
+                            int32_t block_rows, uint8_t* dst, float* scales, void* stream);
+
+/* Workspace kinds for moe_workspace_bytes */
+#define MOE_WS_DISPATCH 1
+#define MOE_WS_FFN 2
+
+/* Bytes of workspace a call needs for this configuration (0 on an invalid cfg). */
+size_t moe_workspace_bytes(const moe_cfg* cfg, int which);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects bad arguments on the host before touching a device (runs without a GPU)."""
+import ctypes
+
+import pytest
+
+from biased_top_routing_amd import _lib as L
+from workloads import MID, TINY, V3_FP8, V3_PREFILL
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_exports_every_header_function(lib):
+    names = L.header_functions()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_update_bias"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert L.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, -5):
+        assert len(L.status_string(st)) >= 2
+
+
+def _cfg(**kw):
+    return L.cfg_from(MID, **kw)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(E=65), L.MOE_ERR_SHAPE),            # E % G
+    (dict(G=0), L.MOE_ERR_SHAPE),
+    (dict(M=9), L.MOE_ERR_SHAPE),             # M > G
+    (dict(k=33), L.MOE_ERR_SHAPE),
+    (dict(k=25, M=3), L.MOE_ERR_SHAPE),       # k > M * E/G = 24
+    (dict(group_topr=0), L.MOE_ERR_SHAPE),
+    (dict(group_topr=9), L.MOE_ERR_SHAPE),
+    (dict(E=1024, G=8), L.MOE_ERR_SHAPE),
+    (dict(H=2047), L.MOE_ERR_SHAPE),
+    (dict(I=1400), L.MOE_ERR_SHAPE),          # bf16 needs I % 128
+    (dict(act="f32"), L.MOE_ERR_UNSUPPORTED),  # f32 act with bf16 weights
+    (dict(bias_eq_mode=2), L.MOE_ERR_UNSUPPORTED),
+    (dict(T=-1), L.MOE_ERR_SHAPE),
+])
+def test_bad_config_rejected_everywhere(kw, status):
+    cfg = _cfg(**kw)
+    assert L.moe_workspace_bytes(cfg, L.MOE_WS_FFN) == 0
+    with pytest.raises(L.MoeError) as e:
+        L.moe_route(cfg, 1, 1, None, 1, 1, 0, 1, 1, stream=0)
+    assert e.value.status == status
+    with pytest.raises(L.MoeError) as e:
+        L.moe_update_bias(cfg, 1, 1, 1e-3, stream=0)
+    assert e.value.status == status
+
+
+def test_null_pointers_rejected():
+    cfg = _cfg()
+    with pytest.raises(L.MoeError) as e:
+        L.moe_route(cfg, None, 1, None, 1, 1, 0, 1, 1, stream=0)          # x needed without SCORES_IN
+    assert e.value.status == L.MOE_ERR_NULL
+    with pytest.raises(L.MoeError) as e:
+        L.moe_route(cfg, None, None, None, None, 1, L.MOE_SCORES_IN, 1, 1, stream=0)   # bias
+    assert e.value.status == L.MOE_ERR_NULL
+    with pytest.raises(L.MoeError) as e:
+        L.moe_combine(cfg, 1, None, 1, 1, 1, stream=0)                     # S > 0 needs y_shared
+    assert e.value.status == L.MOE_ERR_NULL
+    w = L.MoeExpertWeights(1, 1, None, None, None, None, None, None)
+    with pytest.raises(L.MoeError) as e:
+        L.lib()  # ensure loaded
+        st = L.lib().moe_expert_ffn(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, 1, 1 << 40, 0, None)
+        L._check("moe_expert_ffn", st)
+    assert e.value.status == L.MOE_ERR_NULL                                # shared weights missing
+
+
+def test_workspace_too_small_rejected():
+    cfg = _cfg()
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_DISPATCH)
+    st = L.lib().moe_dispatch(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, 1, None, 1, need - 1, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    w = L.MoeExpertWeights(1, 1, None, None, 1, 1, None, None)
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN)
+    st = L.lib().moe_expert_ffn(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, 1, need - 1, 0, None)
+    assert st == L.MOE_ERR_WORKSPACE
+    st = L.lib().moe_expert_ffn(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, 1, need, 7, None)
+    assert st == L.MOE_ERR_UNSUPPORTED                                     # bad phase
+
+
+def test_fp8_needs_scales():
+    cfg = L.cfg_from(V3_FP8)
+    st = L.lib().moe_dispatch(ctypes.byref(cfg), 1, 1, 1, 1, 1, 1, 1, None, 1, 1 << 40, None)
+    assert st == L.MOE_ERR_NULL
+    assert L.lib().moe_quantize_fp8(1, 1, 128, 100, 128, 1, 1, None) == L.MOE_ERR_SHAPE
+    assert L.lib().moe_quantize_fp8(1, 1, 100, 128, 128, 1, 1, None) == L.MOE_ERR_SHAPE
+    assert L.lib().moe_quantize_fp8(1, 1, 128, 128, 64, 1, 1, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_scale_with_tokens():
+    small = L.moe_workspace_bytes(L.cfg_from(V3_PREFILL, T=128), L.MOE_WS_FFN)
+    big = L.moe_workspace_bytes(L.cfg_from(V3_PREFILL), L.MOE_WS_FFN)
+    assert 0 < small < big
+    assert L.moe_workspace_bytes(L.cfg_from(TINY), L.MOE_WS_DISPATCH) >= 256
