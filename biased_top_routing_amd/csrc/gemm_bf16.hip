@@ -30,6 +30,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 enum { kRouter = 0, kGateUp = 1, kDown = 2 };
 
+// K depth of the LDS stages (compile-time tuning knobs)
+#ifndef MOE_GATEUP_BK
+#define MOE_GATEUP_BK 64
+#endif
+#ifndef MOE_DOWN_BK
+#define MOE_DOWN_BK 64
+#endif
+
 struct GemmParams {
   const bf16_t* a_routed;   // gate/up: x_perm [P,H]; down: h_perm [P,I]
   const bf16_t* a_shared;   // gate/up and router: x [T,H]; down: h_shared [T,S*I]
@@ -42,6 +50,14 @@ struct GemmParams {
   const int32_t* ntiles;
   int T, H, E, S, I;
 };
+
+// s_waitcnt immediate that waits until at most N vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima; gfx9
+// encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+constexpr int kVmWaitOneStage() {
+  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
 
 // Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per row).
 template <int CPR>
@@ -58,7 +74,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   constexpr int A_CH = BM * CPR / 256;    // A chunks loaded per thread per K step
   constexpr int B_CH = BN * CPR / 256;
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
-  __shared__ __attribute__((aligned(16))) bf16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[3 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -112,42 +128,38 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     seg_kstride = (int64_t)p.H * p.I;
   }
 
-  int a_off[A_CH], a_lds[A_CH], b_off[B_CH], b_lds[B_CH];
+  // Direct-to-LDS loads: one global_load_lds_dwordx4 fills 1 KB of LDS, lane l
+  // at +16*l.  Instruction i of wave w covers chunks [(i*4 + w)*64, +64) of the
+  // A (or B) region; the lane loads the logical chunk that the XOR swizzle
+  // places at its physical position.
+  int a_off[A_CH], b_off[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
-    a_off[i] = min(r, rows - 1) * lda + c * 8;
-    a_lds[i] = r * BK + swz<CPR>(r, c) * 8;
+    const int q = (i * 4 + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
+    a_off[i] = min(r, rows - 1) * lda + swz<CPR>(r, pc) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int q = tid + 256 * i, r = q / CPR, c = q % CPR;
+    const int q = (i * 4 + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int wrow;
     if constexpr (MODE == kRouter) wrow = min(nt * BN + r, p.E - 1);
     else if constexpr (MODE == kGateUp) wrow = r < 128 ? r : p.I + (r - 128);
     else wrow = min(nt * BN + r, p.H - 1);
-    b_off[i] = wrow * ldw + c * 8;
-    b_lds[i] = BM * BK + r * BK + swz<CPR>(r, c) * 8;
+    b_off[i] = wrow * ldw + swz<CPR>(r, pc) * 8;
   }
-
-  uint4 ra[A_CH], rb[B_CH];
-#define MOE_GLOAD(k0_)                                                                        \
-  {                                                                                           \
-    const int k0v = (k0_);                                                                    \
-    const bf16_t* Wk = W + (MODE == kDown ? (int64_t)(k0v / p.I) * seg_kstride + (k0v % p.I)  \
-                                          : (int64_t)k0v);                                    \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                          \
-        ra[i] = *reinterpret_cast<const uint4*>(A + a_off[i] + k0v);                          \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                          \
-        rb[i] = *reinterpret_cast<const uint4*>(Wk + b_off[i]);                               \
-  }
-#define MOE_LSTORE(buf_)                                                                      \
-  {                                                                                           \
-    bf16_t* sbase = lds + (buf_) * STAGE;                                                     \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                          \
-        *reinterpret_cast<uint4*>(sbase + a_lds[i]) = ra[i];                                  \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                          \
-        *reinterpret_cast<uint4*>(sbase + b_lds[i]) = rb[i];                                  \
+  typedef __attribute__((address_space(3))) void lds_void_t;
+#define MOE_ISSUE(stage_, k0_)                                                                       \
+  {                                                                                                  \
+    const int k0v = (k0_);                                                                           \
+    const bf16_t* Wk = W + (MODE == kDown ? (int64_t)(k0v / p.I) * seg_kstride + (k0v % p.I)         \
+                                          : (int64_t)k0v);                                           \
+    bf16_t* sb = lds + (stage_) * STAGE;                                                             \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                 \
+        __builtin_amdgcn_global_load_lds((const void*)(A + a_off[i] + k0v),                          \
+                                         (lds_void_t*)(sb + (i * 4 + wave) * 512), 16, 0, 0);        \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
+        __builtin_amdgcn_global_load_lds((const void*)(Wk + b_off[i]),                               \
+                                         (lds_void_t*)(sb + BM * BK + (i * 4 + wave) * 512), 16, 0, 0); \
   }
 
   f32x16_t acc[MI][4];
@@ -168,13 +180,23 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     b_rd[ni] = brow + lr;
   }
 
+  // 3-stage ring: slices kt+1 and kt+2 are in flight while slice kt is multiplied.
   const int nk = K / BK;
-  MOE_GLOAD(0);
-  MOE_LSTORE(0);
-  __syncthreads();
+  MOE_ISSUE(0, 0);
+  if (nk > 1) MOE_ISSUE(1, BK);
+  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    MOE_GLOAD((kt + 1 < nk ? kt + 1 : kt) * BK);   // the last step reloads its own slice
+    // this wave's loads of slice kt are done once at most one slice's loads remain
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<A_CH + B_CH>());
+    else __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<0>());
+    // ... and every wave's; slice kt-1's stage is free again.  A bare barrier
+    // that is also a compiler memory fence: __syncthreads would drain the
+    // loads still in flight (vmcnt(0)).
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + 2 < nk) {
+      const int st = cur == 0 ? 2 : cur - 1;   // (kt + 2) % 3
+      MOE_ISSUE(st, (kt + 2) * BK);
+    }
     const bf16_t* base = lds + cur * STAGE;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -193,9 +215,9 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
         for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (kt + 1 < nk) MOE_LSTORE(cur ^ 1);
-    __syncthreads();
+    cur = cur == 2 ? 0 : cur + 1;
   }
+#undef MOE_ISSUE
 
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] holds C[i][j] with j = lane % 32 and
@@ -236,8 +258,6 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       }
     }
   }
-#undef MOE_GLOAD
-#undef MOE_LSTORE
 }
 
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
@@ -273,7 +293,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, 2, 64>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, 2, MOE_GATEUP_BK>), dim3((unsigned)grid), dim3(256), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -287,7 +307,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max2, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, 2, 64>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, 2, MOE_DOWN_BK>), dim3((unsigned)grid), dim3(256), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
