@@ -25,6 +25,9 @@ moe_status validate_cfg(const moe_cfg* c) {
   if ((int64_t)c->T * c->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if ((int64_t)c->T * c->k * c->H >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
   if (!(c->route_scale == c->route_scale)) return MOE_ERR_SHAPE;   // NaN
+  // one buffer descriptor covers a segment's weights (all shared experts together)
+  if ((int64_t)(c->S > 1 ? c->S : 1) * 2 * c->I * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if ((int64_t)c->E * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (c->act == MOE_F32) {
     if (c->H % 4 || c->I % 4) return MOE_ERR_SHAPE;
   } else if (c->wgt == MOE_BF16) {

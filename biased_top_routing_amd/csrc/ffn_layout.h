@@ -18,9 +18,30 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 }
 
 // ---- expert FFN tiling shared by the tile-table builder and the GEMMs
-constexpr int kBM = 128;        // rows of a GEMM tile (tokens)
-constexpr int kBNH = 128;       // h columns of a gate/up tile (128 gate + 128 up weight rows)
-constexpr int kBN2 = 256;       // output columns of a down tile
+#ifndef MOE_TILE_BM
+#define MOE_TILE_BM 128
+#endif
+constexpr int kBM = MOE_TILE_BM;  // rows of a GEMM tile (tokens)
+// Tile shapes of the grouped GEMMs (compile-time choices):
+// WM, WN wavefronts along tokens / weights; MI, NI MFMA 32x32 blocks per
+// wavefront; BK K-depth of an LDS stage; STAGES ring depth; OCC wavefronts
+// per SIMD the kernel is built for.
+#ifndef MOE_GU_TILE
+#define MOE_GU_TILE 1, 4, 4, 4, 64, 2, 1
+#endif
+#ifndef MOE_DN_TILE
+#define MOE_DN_TILE 1, 4, 4, 4, 64, 2, 1
+#endif
+template <int WM_, int WN_, int MI_, int NI_, int BK_, int STAGES_, int OCC_>
+struct TileCfg {
+  static constexpr int WM = WM_, WN = WN_, MI = MI_, NI = NI_, BK = BK_, STAGES = STAGES_, OCC = OCC_;
+  static constexpr int BM = WM * MI * 32, BN = WN * NI * 32;
+};
+using GateUpTile = TileCfg<MOE_GU_TILE>;
+using DownTile = TileCfg<MOE_DN_TILE>;
+static_assert(GateUpTile::BM == kBM && DownTile::BM == kBM, "row tiles of both GEMMs share the tile table");
+constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
+constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
 
 // One tile of the grouped GEMMs: segment (routed expert e < E, or E = shared),
 // first row in the A operand, valid rows, and the column-tile index.
@@ -39,8 +60,8 @@ struct FfnLayout {
     const int64_t P = pairs(c);
     R = P / kBM + c->E;
     Rs = c->S > 0 ? (c->T + kBM - 1) / kBM : 0;
-    nt1 = c->I / kBNH;
-    nt1s = (int64_t)c->S * c->I / kBNH;
+    nt1 = (c->I + kBNH - 1) / kBNH;
+    nt1s = ((int64_t)c->S * c->I + kBNH - 1) / kBNH;
     nt2 = (c->H + kBN2 - 1) / kBN2;
     max1 = R * nt1 + Rs * nt1s;
     max2 = (R + Rs) * nt2;

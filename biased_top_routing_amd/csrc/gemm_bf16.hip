@@ -30,13 +30,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 enum { kRouter = 0, kGateUp = 1, kDown = 2 };
 
-// K depth of the LDS stages (compile-time tuning knobs)
-#ifndef MOE_GATEUP_BK
-#define MOE_GATEUP_BK 64
-#endif
-#ifndef MOE_DOWN_BK
-#define MOE_DOWN_BK 64
-#endif
 
 struct GemmParams {
   const bf16_t* a_routed;   // gate/up: x_perm [P,H]; down: h_perm [P,I]
@@ -59,6 +52,21 @@ constexpr int kVmWaitOneStage() {
   return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
+constexpr int kBufferWord3 = 0x00020000;
+
+// Raw buffer descriptor over [base, base + bytes), built from wave-uniform
+// values so that it lives in SGPRs.
+#if defined(__HIP_DEVICE_COMPILE__)   // the descriptor type exists only for the GPU target
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferWord3);
+}
+#endif
+
 // Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per row).
 template <int CPR>
 __device__ __forceinline__ int swz(int r, int c) {
@@ -66,18 +74,42 @@ __device__ __forceinline__ int swz(int r, int c) {
   else return c ^ (((r >> 1) ^ (r >> 2)) & 3);   // CPR == 4
 }
 
-template <int MODE, int MI, int BK>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
-  constexpr int BM = 2 * MI * 32;
-  constexpr int BN = 256;
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<N>());
+}
+
+// Waits until at most `n` slices' loads (PER instructions each) of this wave
+// are outstanding; n < 4.
+template <int PER>
+__device__ __forceinline__ void wait_slices(int n) {
+  if (n <= 0) wait_vm<0>();
+  else if (n == 1) wait_vm<PER>();
+  else if (n == 2) wait_vm<2 * PER>();
+  else wait_vm<3 * PER>();
+}
+
+// Tile of (WM*MI*32) token rows x (WN*NI*32) weight rows; wave (wm, wn) owns
+// MI x NI MFMA 32x32 blocks.  K advances BK columns per slice through a ring of
+// STAGES LDS stages filled by direct-to-LDS loads.
+template <int MODE, int WM, int WN, int MI, int NI, int BK, int STAGES, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(WM * WN == 4, "four wavefronts per workgroup");
+  constexpr int BM = WM * MI * 32;
+  constexpr int BN = WN * NI * 32;
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
-  constexpr int A_CH = BM * CPR / 256;    // A chunks loaded per thread per K step
+  constexpr int A_CH = BM * CPR / 256;    // direct-to-LDS loads per thread per slice
   constexpr int B_CH = BN * CPR / 256;
+  constexpr int PER = A_CH + B_CH;
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
-  __shared__ __attribute__((aligned(16))) bf16_t lds[3 * STAGE];
+  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "whole loads per thread");
+  static_assert(MODE != kGateUp || BN / 2 == kBNH, "gate/up tile width");
+  static_assert(MODE != kDown || BN == kBN2, "down tile width");
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+  __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // ------------------------------------------------------------ which tile
   int seg = 0, row0, rows, nt;
@@ -86,14 +118,18 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
     rows = min(BM, p.T - row0);
     nt = blockIdx.y;
   } else {
-    const int n_real = *p.ntiles;
+    const int n_real = __builtin_amdgcn_readfirstlane(*p.ntiles);
     const int per = (n_real + 7) >> 3;
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     if (j >= per) return;
     const int L = xcd * per + j;
     if (L >= n_real) return;
     const TileDesc d = p.tiles[L];
-    seg = d.seg; row0 = d.row0; rows = d.rows; nt = d.nt;
+    // the descriptor is the same for the whole workgroup: keep it in SGPRs
+    seg = __builtin_amdgcn_readfirstlane(d.seg);
+    row0 = __builtin_amdgcn_readfirstlane(d.row0);
+    rows = __builtin_amdgcn_readfirstlane(d.rows);
+    nt = __builtin_amdgcn_readfirstlane(d.nt);
   }
   const bool shared = (MODE != kRouter) && seg == p.E;
 
@@ -113,25 +149,27 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   const bf16_t* W;
   int ldw;
   int64_t seg_kstride = 0;   // down, shared: next shared expert's W_d every I columns of K
+  int ncols;                 // valid output columns of this GEMM (h columns for gate/up)
   if constexpr (MODE == kRouter) {
     W = p.w_routed;
     ldw = p.H;
+    ncols = p.E;
   } else if constexpr (MODE == kGateUp) {
-    const int n0 = nt * kBNH;
-    const int sexp = n0 / p.I, c0 = n0 % p.I;
-    W = (shared ? p.w_shared : p.w_routed + (int64_t)seg * 2 * p.I * p.H) +
-        ((int64_t)sexp * 2 * p.I + c0) * p.H;
+    W = shared ? p.w_shared : p.w_routed + (int64_t)seg * 2 * p.I * p.H;
     ldw = p.H;
+    ncols = shared ? p.S * p.I : p.I;
   } else {
     W = shared ? p.w_shared : p.w_routed + (int64_t)seg * p.H * p.I;
     ldw = p.I;
     seg_kstride = (int64_t)p.H * p.I;
+    ncols = p.H;
   }
 
   // Direct-to-LDS loads: one global_load_lds_dwordx4 fills 1 KB of LDS, lane l
   // at +16*l.  Instruction i of wave w covers chunks [(i*4 + w)*64, +64) of the
   // A (or B) region; the lane loads the logical chunk that the XOR swizzle
-  // places at its physical position.
+  // places at its physical position.  Rows past the valid range are clamped
+  // (their results are never stored).
   int a_off[A_CH], b_off[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
@@ -142,80 +180,121 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
   for (int i = 0; i < B_CH; ++i) {
     const int q = (i * 4 + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int wrow;
-    if constexpr (MODE == kRouter) wrow = min(nt * BN + r, p.E - 1);
-    else if constexpr (MODE == kGateUp) wrow = r < 128 ? r : p.I + (r - 128);
-    else wrow = min(nt * BN + r, p.H - 1);
+    if constexpr (MODE == kGateUp) {
+      // rows [0, BN/2) gate, [BN/2, BN) up, of h columns nt*BN/2 + j
+      const bool up = r >= BN / 2;
+      const int c = min(nt * (BN / 2) + (up ? r - BN / 2 : r), ncols - 1);
+      wrow = (c / p.I) * 2 * p.I + (up ? p.I : 0) + c % p.I;
+    } else {
+      wrow = min(nt * BN + r, ncols - 1);
+    }
     b_off[i] = wrow * ldw + swz<CPR>(r, pc) * 8;
   }
+  // Buffer descriptors over this tile's A rows and this segment's weights: the
+  // per-lane part of every address is a 32-bit byte offset, the K advance an
+  // SGPR offset.  Accesses past the described range read as zero.
+  // (the host checks that a segment's weights stay below 2 GiB)
+  int w_bytes;
+  if constexpr (MODE == kRouter) w_bytes = p.E * p.H * 2;
+  else if constexpr (MODE == kGateUp) w_bytes = (shared ? p.S : 1) * 2 * p.I * p.H * 2;
+  else w_bytes = (shared ? p.S : 1) * p.H * p.I * 2;
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, rows * lda * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(W, w_bytes);
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) a_off[i] *= 2;
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) b_off[i] *= 2;
   typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_ISSUE(stage_, k0_)                                                                       \
   {                                                                                                  \
     const int k0v = (k0_);                                                                           \
-    const bf16_t* Wk = W + (MODE == kDown ? (int64_t)(k0v / p.I) * seg_kstride + (k0v % p.I)         \
-                                          : (int64_t)k0v);                                           \
+    const int wk = MODE == kDown ? (int)((k0v / p.I) * seg_kstride) + (k0v % p.I) : k0v;             \
     bf16_t* sb = lds + (stage_) * STAGE;                                                             \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                 \
-        __builtin_amdgcn_global_load_lds((const void*)(A + a_off[i] + k0v),                          \
-                                         (lds_void_t*)(sb + (i * 4 + wave) * 512), 16, 0, 0);        \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sb + (i * 4 + wave) * 512), 16, \
+                                                 a_off[i], k0v * 2, 0, 0);                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
-        __builtin_amdgcn_global_load_lds((const void*)(Wk + b_off[i]),                               \
-                                         (lds_void_t*)(sb + BM * BK + (i * 4 + wave) * 512), 16, 0, 0); \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w,                                             \
+                                                 (lds_void_t*)(sb + BM * BK + (i * 4 + wave) * 512), \
+                                                 16, b_off[i], wk * 2, 0, 0);                        \
   }
 
-  f32x16_t acc[MI][4];
+  f32x16_t acc[MI][NI];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
 
-  int a_rd[MI], b_rd[4];
+  // LDS rows this lane reads for its MFMA operands
+  int a_rd[MI], b_rd[NI];
   const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) a_rd[mi] = wm * MI * 32 + mi * 32 + lr;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const int brow = (MODE == kGateUp) ? (ni >> 1) * 128 + wn * 64 + (ni & 1) * 32 : wn * 128 + ni * 32;
+  for (int ni = 0; ni < NI; ++ni) {
+    int brow;
+    if constexpr (MODE == kGateUp) {
+      constexpr int HALF = NI / 2;   // gate blocks, then the matching up blocks
+      brow = (ni < HALF ? 0 : BN / 2) + wn * HALF * 32 + (ni % HALF) * 32;
+    } else {
+      brow = wn * NI * 32 + ni * 32;
+    }
     b_rd[ni] = brow + lr;
   }
 
-  // 3-stage ring: slices kt+1 and kt+2 are in flight while slice kt is multiplied.
+  // Ring: slices kt+1 .. kt+STAGES-2 are in flight while slice kt is multiplied.
   const int nk = K / BK;
-  MOE_ISSUE(0, 0);
-  if (nk > 1) MOE_ISSUE(1, BK);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) MOE_ISSUE(s, s * BK);
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads of slice kt are done once at most one slice's loads remain
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<A_CH + B_CH>());
-    else __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<0>());
-    // ... and every wave's; slice kt-1's stage is free again.  A bare barrier
-    // that is also a compiler memory fence: __syncthreads would drain the
-    // loads still in flight (vmcnt(0)).
+    // this wave's loads of slice kt have landed once only the later slices remain
+    wait_slices<PER>(min(nk - 1, kt + STAGES - 2) - kt);
+    // ... and every wave's; the stage of slice kt-1 is free again.  A bare
+    // barrier that is also a compiler memory fence: __syncthreads would drain
+    // the loads still in flight (vmcnt(0)).
     asm volatile("s_barrier" ::: "memory");
-    if (kt + 2 < nk) {
-      const int st = cur == 0 ? 2 : cur - 1;   // (kt + 2) % 3
-      MOE_ISSUE(st, (kt + 2) * BK);
+    if (kt + STAGES - 1 < nk) {
+      const int st = cur == 0 ? STAGES - 1 : cur - 1;   // (kt + STAGES - 1) % STAGES
+      MOE_ISSUE(st, (kt + STAGES - 1) * BK);
     }
     const bf16_t* base = lds + cur * STAGE;
+    // Operand fragments are double-buffered across the BK/16 MFMA k-steps: the
+    // reads of step kk+1 are interleaved with the MFMAs of step kk.
+    constexpr int KK = BK / 16;
+    bf16x8_t fa[2][MI], fb[2][NI];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + kh;
-      bf16x8_t a[MI], b[4];
+    for (int mi = 0; mi < MI; ++mi)
+      fa[0][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + swz<CPR>(a_rd[mi], kh) * 8);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      fb[0][ni] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + b_rd[ni] * BK + swz<CPR>(b_rd[ni], kh) * 8);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk + 1 < KK) {
+        const int c = (kk + 1) * 2 + kh;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          fa[nb][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + swz<CPR>(a_rd[mi], c) * 8);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          fb[nb][ni] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + b_rd[ni] * BK +
+                                                          swz<CPR>(b_rd[ni], c) * 8);
+      }
+      // the reads above stay ahead of this step's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
-        a[mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + swz<CPR>(a_rd[mi], c) * 8);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        b[ni] = *reinterpret_cast<const bf16x8_t*>(base + BM * BK + b_rd[ni] * BK +
-                                                   swz<CPR>(b_rd[ni], c) * 8);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc[mi][ni], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
 #undef MOE_ISSUE
 
@@ -230,34 +309,36 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmParams p) {
       if (i >= rows) continue;
       const int64_t row = row0 + i;
       if constexpr (MODE == kGateUp) {
-        const int ldo = shared ? p.S * p.I : p.I;
+        constexpr int HALF = NI / 2;
         bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const float g = acc[mi][ni][r], u = acc[mi][ni + 2][r];
+        for (int ni = 0; ni < HALF; ++ni) {
+          const int col = nt * (BN / 2) + wn * HALF * 32 + ni * 32 + lr;
+          const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
           const float h = g / (1.0f + __expf(-g)) * u;
-          out[row * ldo + nt * kBNH + wn * 64 + ni * 32 + lr] = f32_to_bf16(h);
+          if (col < ncols) out[row * ncols + col] = f32_to_bf16(h);
         }
       } else if constexpr (MODE == kDown) {
         bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = nt * BN + wn * 128 + ni * 32 + lr;
-          if (col < p.H) out[row * p.H + col] = f32_to_bf16(acc[mi][ni][r]);
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = nt * BN + wn * NI * 32 + ni * 32 + lr;
+          if (col < ncols) out[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
         }
       } else {
         float* out = static_cast<float*>(p.out_routed);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const int col = nt * BN + wn * 128 + ni * 32 + lr;
-          if (col < p.E) {
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = nt * BN + wn * NI * 32 + ni * 32 + lr;
+          if (col < ncols) {
             const float l = acc[mi][ni][r] + (p.offset ? p.offset[col] : 0.f);
-            out[row * p.E + col] = 1.0f / (1.0f + expf(-l));
+            out[row * ncols + col] = 1.0f / (1.0f + expf(-l));
           }
         }
       }
     }
   }
+#endif
 }
 
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
@@ -269,7 +350,7 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   p.out_routed = scores;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
   const dim3 grid((unsigned)((c->T + 63) / 64), (unsigned)((c->E + 255) / 256));
-  hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, 1, 64>), grid, dim3(256), 0, st, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, 2, 2, 1, 4, 64, 3, 1>), grid, dim3(256), 0, st, p);
   return launch_status();
 }
 
@@ -293,7 +374,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, 2, MOE_GATEUP_BK>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid), dim3(256), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -307,7 +388,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max2, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, 2, MOE_DOWN_BK>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DN_TILE>), dim3((unsigned)grid), dim3(256), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
