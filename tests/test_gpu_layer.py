@@ -107,7 +107,9 @@ def _check_full_route(c, s_ora, bias, idx_gpu):
     """Own-scores routing check: mismatches only at near-ties of the oracle."""
     idx_o, _ = oracle.route(s_ora, bias, c.G, c.M, c.k, c.group_topr, c.route_scale)
     gk, gm = oracle.route_diagnostics(s_ora, bias, c.G, c.M, c.k, c.group_topr)
-    bad = (idx_o != idx_gpu).any(axis=1)
+    # the selected set may differ only at a near-tie (slot order within a set may differ
+    # wherever two selected scores are within rounding of each other)
+    bad = (np.sort(idx_o, axis=1) != np.sort(idx_gpu, axis=1)).any(axis=1)
     assert ((gk[bad] < GAP) | (gm[bad] < GAP)).all()
     return int(bad.sum())
 
