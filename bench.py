@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--workload", default="v3_prefill_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this size 3 times (a plain copy kernel of known "
+                         "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -54,6 +57,37 @@ def stage_bytes(c):
     dispatch = c.T * c.H * a + c.T * c.k * c.H * a + c.T * c.k * 4 * 4   # x in, x_perm out, idx in, perm/inv out
     combine = c.T * c.k * c.H * a + c.T * c.H * a * (2 if c.S else 1) + c.T * c.k * 8
     return dict(router=router, topk=route, dispatch=dispatch, combine=combine)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gate_up_v3_prefill_bf16.txt")
+TRAFFIC_SOURCES = ["include/moe.h", "biased_top_routing_amd/csrc/common.h", "biased_top_routing_amd/csrc/ffn_layout.h",
+                   "biased_top_routing_amd/csrc/ffn.hip", "biased_top_routing_amd/csrc/gemm_bf16.hip"]
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up GEMM from the committed counter summary, or None
+    when the summary is missing, covers another workload, or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith(" "))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("workload") != workload or kv.get("sources_sha256") != sources_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(c, x, w, bias, budget_s):
@@ -180,6 +214,15 @@ def main():
     value = c.T / (wall / args.steps)
     counts = layer.counts.cpu().numpy()
     log(f"{ms_per_step:.3f} ms/step, {value:,.0f} tokens/s; stages {stage_ms}")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        del src, dst
 
     gu_flops = c.gate_up_flops()
     dn_flops = c.down_flops()
@@ -210,7 +253,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(c.name),
             "flops_per_launch": gu_flops,
             "avg_launch_ms": round(stage_ms["gate_up"], 4),
         },
