@@ -20,6 +20,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORES_IN = 1
 MOE_FFN_ALL, MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1, 2
 MOE_WS_DISPATCH, MOE_WS_FFN = 1, 2
+MOE_WSP_H, MOE_WSP_H_SCALE, MOE_WSP_H_SHARED, MOE_WSP_H_SHARED_SCALE = 0, 1, 2, 3
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 
 
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_update_bias": [cfgp, vp, vp, f32, vp],
             "moe_quantize_fp8": [vp, i32, i32, i32, i32, vp, vp, vp],
+            "moe_ffn_workspace_part": [cfgp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -163,6 +165,14 @@ def moe_update_bias(cfg, counts, bias, gamma, stream=None):
 def moe_quantize_fp8(src, n_mat, rows, cols, block_rows, dst, scales, stream=None):
     _check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(src), n_mat, rows, cols, block_rows, _p(dst),
                                                       _p(scales), _s(stream)))
+
+
+def moe_ffn_workspace_part(cfg, part) -> tuple:
+    """(byte offset, byte size) of an intermediate inside the moe_expert_ffn workspace."""
+    off, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("moe_ffn_workspace_part", lib().moe_ffn_workspace_part(ctypes.byref(cfg), part, ctypes.byref(off),
+                                                                  ctypes.byref(nb)))
+    return int(off.value), int(nb.value)
 
 
 def moe_workspace_bytes(cfg, which) -> int:

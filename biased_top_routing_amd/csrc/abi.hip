@@ -32,8 +32,10 @@ moe_status validate_cfg(const moe_cfg* c) {
     if (c->H % 4 || c->I % 4) return MOE_ERR_SHAPE;
   } else if (c->wgt == MOE_BF16) {
     if (c->H % 64 || c->I % 128) return MOE_ERR_SHAPE;
-  } else {  // fp8 experts
+  } else {  // fp8 experts: K of every GEMM at most kFp8MaxKC chunks of 128
     if (c->H % 128 || c->I % 128) return MOE_ERR_SHAPE;
+    if (c->H > 128 * kFp8MaxKC || (int64_t)(c->S > 1 ? c->S : 1) * c->I > 128 * kFp8MaxKC)
+      return MOE_ERR_SHAPE;
   }
   return MOE_OK;
 }
@@ -47,6 +49,21 @@ extern "C" size_t moe_workspace_bytes(const moe_cfg* cfg, int which) {
   if (which == MOE_WS_DISPATCH) return dispatch_ws_bytes(cfg);
   if (which == MOE_WS_FFN) return FfnLayout(cfg).total;
   return 0;
+}
+
+extern "C" moe_status moe_ffn_workspace_part(const moe_cfg* cfg, int part, size_t* offset, size_t* bytes) {
+  const moe_status st = validate_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (!offset || !bytes) return MOE_ERR_NULL;
+  const FfnLayout L(cfg);
+  switch (part) {
+    case MOE_WSP_H: *offset = L.off_hp; *bytes = L.off_hps - L.off_hp; break;
+    case MOE_WSP_H_SCALE: *offset = L.off_hps; *bytes = L.off_hs - L.off_hps; break;
+    case MOE_WSP_H_SHARED: *offset = L.off_hs; *bytes = L.off_hss - L.off_hs; break;
+    case MOE_WSP_H_SHARED_SCALE: *offset = L.off_hss; *bytes = L.off_xq - L.off_hss; break;
+    default: return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
 }
 
 extern "C" const char* moe_status_string(moe_status s) {

@@ -42,6 +42,11 @@ using DownTile = TileCfg<MOE_DN_TILE>;
 static_assert(GateUpTile::BM == kBM && DownTile::BM == kBM, "row tiles of both GEMMs share the tile table");
 constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
 constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
+// FP8 GEMMs: 128 h columns (one 1 x 128 quantisation tile of h) per gate/up
+// tile, 256 output columns per down tile, K at most kFp8MaxKC chunks of 128.
+constexpr int kFp8BNH = 128;
+constexpr int kFp8BN2 = 256;
+constexpr int kFp8MaxKC = 64;
 
 // One tile of the grouped GEMMs: segment (routed expert e < E, or E = shared),
 // first row in the A operand, valid rows, and the column-tile index.
@@ -60,9 +65,11 @@ struct FfnLayout {
     const int64_t P = pairs(c);
     R = P / kBM + c->E;
     Rs = c->S > 0 ? (c->T + kBM - 1) / kBM : 0;
-    nt1 = (c->I + kBNH - 1) / kBNH;
-    nt1s = ((int64_t)c->S * c->I + kBNH - 1) / kBNH;
-    nt2 = (c->H + kBN2 - 1) / kBN2;
+    const bool f8 = c->wgt == MOE_FP8_E4M3;
+    const int bnh = f8 ? kFp8BNH : kBNH, bn2 = f8 ? kFp8BN2 : kBN2;
+    nt1 = (c->I + bnh - 1) / bnh;
+    nt1s = ((int64_t)c->S * c->I + bnh - 1) / bnh;
+    nt2 = (c->H + bn2 - 1) / bn2;
     max1 = R * nt1 + Rs * nt1s;
     max2 = (R + Rs) * nt2;
     hbytes = c->wgt == MOE_FP8_E4M3 ? 1 : (int)act_bytes(c);

@@ -216,6 +216,23 @@ moe_status moe_quantize_fp8(const void* src_bf16, int32_t n_mat, int32_t rows, i
 /* Bytes of workspace a call needs for this configuration (0 on an invalid cfg). */
 size_t moe_workspace_bytes(const moe_cfg* cfg, int which);
 
+/*
+ * moe_ffn_workspace_part - where moe_expert_ffn keeps the SwiGLU intermediate h
+ * inside its workspace, so that a caller can read it after MOE_FFN_GATE_UP (or
+ * supply it before MOE_FFN_DOWN).  Parts:
+ *   MOE_WSP_H               h of the routed rows [T*k, I], act dtype or E4M3
+ *   MOE_WSP_H_SCALE         their 1x128 tile scales [T*k, I/128] fp32 (FP8 only)
+ *   MOE_WSP_H_SHARED        h of the shared experts [T, S*I]
+ *   MOE_WSP_H_SHARED_SCALE  their scales [T, S*I/128] fp32 (FP8 only)
+ * Writes the byte offset from the start of the workspace and the byte size
+ * (0 for a part this configuration does not hold).  Host only; no device call.
+ */
+#define MOE_WSP_H 0
+#define MOE_WSP_H_SCALE 1
+#define MOE_WSP_H_SHARED 2
+#define MOE_WSP_H_SHARED_SCALE 3
+moe_status moe_ffn_workspace_part(const moe_cfg* cfg, int part, size_t* offset, size_t* bytes);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -51,11 +51,18 @@ class _Fp8Expert:
         self.qd, self.sd = quantize_blocks_128x128(decode_act(w_down))
         self.I = self.qgu.shape[0] // 2
 
-    def __call__(self, qx, sx):
+    def hidden(self, qx, sx):
+        """SwiGLU intermediate h (fp64) of rows given as 1x128 E4M3 tiles."""
         ab = fp8_matmul(qx, sx, self.qgu, self.sgu)
-        h = _silu_mul(ab[:, :self.I], ab[:, self.I:])
-        qh, sh = quantize_rows_1x128(h.astype(F32))
+        return _silu_mul(ab[:, :self.I], ab[:, self.I:])
+
+    def down(self, qh, sh):
+        """Down projection of an E4M3-quantised h (fp64)."""
         return fp8_matmul(qh, sh, self.qd, self.sd)
+
+    def __call__(self, qx, sx):
+        qh, sh = quantize_rows_1x128(self.hidden(qx, sx).astype(F32))
+        return self.down(qh, sh)
 
 
 def _expert_fn(cfg, w_gate_up, w_down):

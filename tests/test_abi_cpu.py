@@ -102,3 +102,26 @@ def test_workspace_sizes_scale_with_tokens():
     big = L.moe_workspace_bytes(L.cfg_from(V3_PREFILL), L.MOE_WS_FFN)
     assert 0 < small < big
     assert L.moe_workspace_bytes(L.cfg_from(TINY), L.MOE_WS_DISPATCH) >= 256
+
+
+def test_ffn_workspace_parts():
+    """The h parts lie inside the FFN workspace, do not overlap and have the sizes the
+    header states; scale parts are empty unless the experts are FP8."""
+    for c in (MID, V3_PREFILL, V3_FP8):
+        cfg = L.cfg_from(c)
+        total = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN)
+        parts = [L.moe_ffn_workspace_part(cfg, p) for p in
+                 (L.MOE_WSP_H, L.MOE_WSP_H_SCALE, L.MOE_WSP_H_SHARED, L.MOE_WSP_H_SHARED_SCALE)]
+        fp8 = c.wgt == "fp8_e4m3"
+        eb = 1 if fp8 else 2
+        P = c.T * c.k
+        assert parts[0][1] >= P * c.I * eb and parts[2][1] >= c.T * c.S * c.I * eb
+        if fp8:
+            assert parts[1][1] >= P * (c.I // 128) * 4 and parts[3][1] >= c.T * c.S * (c.I // 128) * 4
+        else:
+            assert parts[1][1] == 0 and parts[3][1] == 0
+        spans = sorted((o, o + n) for o, n in parts if n)
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert spans[-1][1] <= total and all(o % 256 == 0 for o, _ in spans)
+    with pytest.raises(L.MoeError):
+        L.moe_ffn_workspace_part(L.cfg_from(MID), 9)
