@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_prefill_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the decode-size and FP8 measurements that follow the headline one")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size 3 times (a plain copy kernel of known "
@@ -143,6 +145,77 @@ def cpu_baseline(c, x, w, bias, budget_s):
             "measured_s": round(t_route + t_routed + t_shared + t_combine, 2)}
 
 
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+STAGES = ["route", "dispatch", "gate_up", "down", "combine", "bias"]
+
+
+def time_layer(layer, x, bias, c, steps, warmup):
+    """Warm up, then time `steps` whole-layer passes.  Returns (ms per step from the
+    host clock, mean ms of each stage from HIP events recorded on the layer's stream)."""
+    import numpy as np
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+
+    def step(ev=None):
+        calls = [lambda: layer.route(x, bias), lambda: layer.dispatch(x),
+                 lambda: layer.expert_ffn(x, L.MOE_FFN_GATE_UP), lambda: layer.expert_ffn(x, L.MOE_FFN_DOWN),
+                 layer.combine, lambda: layer.update_bias(bias, c.gamma)]
+        for j, f in enumerate(calls):
+            if ev is not None:
+                ev[j].record()
+            f()
+        if ev is not None:
+            ev[len(calls)].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j, n in enumerate(STAGES)}
+    return wall * 1e3 / steps, stage_ms
+
+
+def decode_extra(layer, c, w, steps, warmup):
+    """The same layer at decode size (T=128): time per step and the rate at which it
+    streams the weights of the experts it touches (the decode roofline is HBM)."""
+    import torch
+
+    from workloads import CONFIGS
+    from workloads.inputs import make_x
+    cd = CONFIGS["v3_decode_bf16"]
+    layer.alloc(cd.T)
+    x = to_dev(make_x(cd, 0))
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    ms, stage_ms = time_layer(layer, x, bias, cd, steps, warmup)
+    counts = layer.counts.cpu().numpy()
+    touched = int((counts > 0).sum())
+    wbytes = (touched + cd.S) * 3 * cd.H * cd.I * 2 + cd.E * cd.H * 2
+    iobytes = cd.T * cd.H * 2 * (2 + 2 * cd.k)     # x in, y out, x_perm and y_perm written and read
+    return {"workload": cd.name, "T": cd.T, "ms_per_step": round(ms, 4), "tokens_per_s": round(cd.T / (ms * 1e-3), 1),
+            "experts_touched": touched, "hbm_gbs": round((wbytes + iobytes) / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round((wbytes + iobytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes": wbytes + iobytes, "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+
+
+def gemm_summary(c, ms_per_step, stage_ms):
+    peak = PEAK_FP8_TFLOPS if c.wgt == "fp8_e4m3" else PEAK_BF16_TFLOPS
+    gu = c.gate_up_flops() / (stage_ms["gate_up"] * 1e-3) / 1e12
+    dn = c.down_flops() / (stage_ms["down"] * 1e-3) / 1e12
+    return peak, gu, dn
+
+
+def to_dev(a):
+    from biased_top_routing_amd.runner import to_device
+    return to_device(a)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -151,17 +224,15 @@ def main():
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from biased_top_routing_amd import _lib as L
-    from biased_top_routing_amd.runner import MoeLayerGPU, to_device
+    from biased_top_routing_amd.runner import MoeLayerGPU
     from workloads import CONFIGS
     from workloads.inputs import make_weights, make_x
 
     L.lib()     # fails loudly without the built library
     c = CONFIGS[args.workload]
-    assert c.wgt == "bf16", "the headline bench is the bf16 workload"
     torch.cuda.set_device(0)
     log(f"workload {c.name}: generating seeded inputs")
     t0 = time.perf_counter()
@@ -169,49 +240,12 @@ def main():
     xh = make_x(c, 0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     layer = MoeLayerGPU(c, w)
-    x = to_device(xh)
+    x = to_dev(xh)
     bias = torch.from_numpy(w.bias0.copy()).cuda()
     torch.cuda.synchronize()
-    log("uploaded; warming up")
-
-    names = ["route", "dispatch", "gate_up", "down", "combine", "bias"]
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        layer.route(x, bias)
-        if ev is not None:
-            ev[1].record()
-        layer.dispatch(x)
-        if ev is not None:
-            ev[2].record()
-        layer.expert_ffn(x, L.MOE_FFN_GATE_UP)
-        if ev is not None:
-            ev[3].record()
-        layer.expert_ffn(x, L.MOE_FFN_DOWN)
-        if ev is not None:
-            ev[4].record()
-        layer.combine()
-        if ev is not None:
-            ev[5].record()
-        layer.update_bias(bias, c.gamma)
-        if ev is not None:
-            ev[6].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage_ms = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) for j, n in enumerate(names)}
-    ms_per_step = wall * 1e3 / args.steps
-    value = c.T / (wall / args.steps)
+    log(f"uploaded; timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms_per_step, stage_ms = time_layer(layer, x, bias, c, args.steps, args.warmup)
+    value = c.T / (ms_per_step * 1e-3)
     counts = layer.counts.cpu().numpy()
     log(f"{ms_per_step:.3f} ms/step, {value:,.0f} tokens/s; stages {stage_ms}")
     if args.copy_calibration_mib:
@@ -224,13 +258,11 @@ def main():
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
 
-    gu_flops = c.gate_up_flops()
-    dn_flops = c.down_flops()
-    gu_tflops = gu_flops / (stage_ms["gate_up"] * 1e-3) / 1e12
-    dn_tflops = dn_flops / (stage_ms["down"] * 1e-3) / 1e12
-    total_flops = gu_flops + dn_flops + c.router_flops()
+    peak, gu_tflops, dn_tflops = gemm_summary(c, ms_per_step, stage_ms)
+    total_flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
     b = stage_bytes(c)
     route_gbs = (b["router"] + b["topk"]) / (stage_ms["route"] * 1e-3) / 1e9
+    fp8 = c.wgt == "fp8_e4m3"
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -242,19 +274,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3 experts, bf16 router" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": c.name, "T": c.T, "H": c.H, "E": c.E, "G": c.G, "M": c.M, "k": c.k, "S": c.S,
                    "I": c.I, "route_scale": c.route_scale, "parallelism": "single-gpu"},
         "roofline": {
-            "kernel": "gemm_bf16_kernel<gate_up> (routed + shared gate/up GEMM with fused SwiGLU)",
+            "kernel": ("gemm_fp8_kernel<gate_up>" if fp8 else "gemm_bf16_kernel<gate_up>") +
+                      " (routed + shared gate/up GEMM with fused SwiGLU)",
             "bound": "mfma",
             "achieved": round(gu_tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": measured_traffic(c.name),
-            "flops_per_launch": gu_flops,
+            "frac": round(gu_tflops / peak, 4),
+            "traffic": None if fp8 else measured_traffic(c.name),
+            "flops_per_launch": c.gate_up_flops(),
             "avg_launch_ms": round(stage_ms["gate_up"], 4),
         },
         "stages": {
@@ -268,7 +301,33 @@ def main():
             "max_over_mean_load": round(float(counts.max() / (c.T * c.k / c.E)), 3),
         },
     }
-    if not args.no_cpu_baseline:
+    if not args.no_extras and c.name == "v3_prefill_bf16":
+        extras = {}
+        log("extra: the same layer at decode size")
+        extras["v3_decode_bf16"] = decode_extra(layer, c, w, max(args.steps, 20), args.warmup)
+        del layer, x
+        torch.cuda.empty_cache()
+        cf = CONFIGS["v3_fp8"]
+        log("extra: the FP8 layer (T=32768, Zipf-skewed routing)")
+        wf = make_weights(cf)
+        lf = MoeLayerGPU(cf, wf)
+        xf = to_dev(make_x(cf, 0))
+        bf = torch.from_numpy(wf.bias0.copy()).cuda()
+        msf, stf = time_layer(lf, xf, bf, cf, args.steps, args.warmup)
+        pk, gu8, dn8 = gemm_summary(cf, msf, stf)
+        cnt = lf.counts.cpu().numpy()
+        extras["v3_fp8"] = {"workload": cf.name, "T": cf.T, "ms_per_step": round(msf, 4),
+                            "tokens_per_s": round(cf.T / (msf * 1e-3), 1),
+                            "gate_up_tflops": round(gu8, 2), "gate_up_frac_fp8_peak": round(gu8 / pk, 4),
+                            "down_tflops": round(dn8, 2), "down_frac_fp8_peak": round(dn8 / pk, 4),
+                            "layer_tflops": round((cf.gate_up_flops() + cf.down_flops() + cf.router_flops()) /
+                                                  (msf * 1e-3) / 1e12, 2),
+                            "max_over_mean_load": round(float(cnt.max() / (cf.T * cf.k / cf.E)), 3),
+                            "stages_ms": {k: round(v, 4) for k, v in stf.items()}}
+        del lf, xf
+        torch.cuda.empty_cache()
+        out["other_workloads"] = extras
+    if not args.no_cpu_baseline and not fp8:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(c, xh, w, w.bias0, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -14,9 +14,13 @@ namespace moe {
 // ------------------------------------------------------------ tile tables
 // Segments 0..E-1 are the routed experts (rows offsets[e]..offsets[e+1] of the
 // permuted rows); segment E is the shared experts over all T tokens.  Each
-// segment contributes ceil(rows / kBM) row tiles times its column tiles,
-// listed column-tile-major so that tiles reading the same weight panel are
-// adjacent.  One workgroup; exclusive prefix sums over segments in LDS.
+// segment contributes ceil(rows / kBM) row tiles times its column tiles.
+// Inside a segment the row tiles are cut into groups of kGroupRowTiles; a
+// group's tiles are listed column-tile-major.  Tiles that run at the same time
+// on one XCD (consecutive entries) then cover a few row tiles times a few
+// column tiles, so both their activation rows and their weight rows are
+// shared in that XCD's L2, also for segments far larger than the number of
+// tiles in flight.  One workgroup; exclusive prefix sums over segments in LDS.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int S, int T, int nt1, int nt1s, int nt2,
                                                            TileDesc* __restrict__ t1,
@@ -74,7 +78,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       while (g + 1 < nseg && pre[g + 1] <= L) ++g;
       const int local = L - pre[g];
       const int mt = mt_s[g];
-      const int nt = local / mt, rt = local % mt;
+      const int ncol = (pass == 0 ? (g < E ? nt1 : nt1s) : nt2);
+      const int q = local / (kGroupRowTiles * ncol);             // row-tile group (all earlier ones full)
+      const int idx = local - q * kGroupRowTiles * ncol;
+      const int gs = min(kGroupRowTiles, mt - q * kGroupRowTiles);
+      const int nt = idx / gs, rt = q * kGroupRowTiles + idx % gs;
       TileDesc d;
       d.seg = g;
       d.row0 = row0_s[g] + rt * kBM;

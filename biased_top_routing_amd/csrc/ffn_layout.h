@@ -48,6 +48,12 @@ constexpr int kFp8BNH = 128;
 constexpr int kFp8BN2 = 256;
 constexpr int kFp8MaxKC = 64;
 
+// Row tiles per group in the tile order of a segment (see build_tiles_kernel).
+#ifndef MOE_GROUP_ROW_TILES
+#define MOE_GROUP_ROW_TILES 8
+#endif
+constexpr int kGroupRowTiles = MOE_GROUP_ROW_TILES;
+
 // One tile of the grouped GEMMs: segment (routed expert e < E, or E = shared),
 // first row in the A operand, valid rows, and the column-tile index.
 struct TileDesc {
