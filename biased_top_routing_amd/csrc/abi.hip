@@ -25,6 +25,8 @@ moe_status validate_cfg(const moe_cfg* c) {
   if ((int64_t)c->T * c->k >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if ((int64_t)c->T * c->k * c->H >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
   if (!(c->route_scale == c->route_scale)) return MOE_ERR_SHAPE;   // NaN
+  // 32-bit byte offsets inside a GEMM tile (up to 257 rows of the widest operand)
+  if (c->H > (1 << 20) || c->I > (1 << 20) || (int64_t)c->S * c->I > (1 << 20)) return MOE_ERR_SHAPE;
   // one buffer descriptor covers a segment's weights (all shared experts together)
   if ((int64_t)(c->S > 1 ? c->S : 1) * 2 * c->I * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if ((int64_t)c->E * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;

@@ -14,7 +14,7 @@ namespace moe {
 // ------------------------------------------------------------ tile tables
 // Segments 0..E-1 are the routed experts (rows offsets[e]..offsets[e+1] of the
 // permuted rows); segment E is the shared experts over all T tokens.  Each
-// segment contributes ceil(rows / kBM) row tiles times its column tiles.
+// segment contributes ceil(rows / bm) row tiles times its column tiles.
 // Inside a segment the row tiles are cut into groups of kGroupRowTiles; a
 // group's tiles are listed column-tile-major.  Tiles that run at the same time
 // on one XCD (consecutive entries) then cover a few row tiles times a few
@@ -22,7 +22,7 @@ namespace moe {
 // shared in that XCD's L2, also for segments far larger than the number of
 // tiles in flight.  One workgroup; exclusive prefix sums over segments in LDS.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int S, int T, int nt1, int nt1s, int nt2,
+                                                           int S, int T, int bm, int nt1, int nt1s, int nt2,
                                                            TileDesc* __restrict__ t1,
                                                            TileDesc* __restrict__ t2,
                                                            int32_t* __restrict__ hdr) {
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   if (tid < nseg) {
     const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : T;
     const int row0 = tid < E ? offsets[tid] : 0;
-    const int mt = (rows + kBM - 1) / kBM;
+    const int mt = (rows + bm - 1) / bm;
     c1 = mt * (tid < E ? nt1 : nt1s);
     c2 = mt * nt2;
     mt_s[tid] = mt;
@@ -85,8 +85,8 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       const int nt = idx / gs, rt = q * kGroupRowTiles + idx % gs;
       TileDesc d;
       d.seg = g;
-      d.row0 = row0_s[g] + rt * kBM;
-      d.rows = min(kBM, rows_s[g] - rt * kBM);
+      d.row0 = row0_s[g] + rt * bm;
+      d.rows = min(bm, rows_s[g] - rt * bm);
       d.nt = nt;
       out[L] = d;
     }
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, c->E, c->S, c->T,
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm,
                      (int)L.nt1, (int)L.nt1s, (int)L.nt2,
                      reinterpret_cast<TileDesc*>(base + L.off_t1),
                      reinterpret_cast<TileDesc*>(base + L.off_t2),

@@ -19,18 +19,20 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 
 // ---- expert FFN tiling shared by the tile-table builder and the GEMMs
 #ifndef MOE_TILE_BM
-#define MOE_TILE_BM 128
+#define MOE_TILE_BM 256
 #endif
-constexpr int kBM = MOE_TILE_BM;  // rows of a GEMM tile (tokens)
+constexpr int kBM = MOE_TILE_BM;  // rows of a bf16 GEMM tile (tokens)
 // Tile shapes of the grouped GEMMs (compile-time choices):
 // WM, WN wavefronts along tokens / weights; MI, NI MFMA 32x32 blocks per
-// wavefront; BK K-depth of an LDS stage; STAGES ring depth; OCC wavefronts
-// per SIMD the kernel is built for.
+// wavefront; BK K-depth of an LDS stage; STAGES ring depth; OCC workgroups
+// per CU the kernel is built for.  Both default to 256 x 256 tiles with two
+// or four wavefronts per SIMD (measured: a second wavefront per SIMD covers
+// the load and barrier waits that a single wavefront exposes).
 #ifndef MOE_GU_TILE
-#define MOE_GU_TILE 1, 4, 4, 4, 64, 2, 1
+#define MOE_GU_TILE 2, 4, 4, 2, 64, 2, 1
 #endif
 #ifndef MOE_DN_TILE
-#define MOE_DN_TILE 1, 4, 4, 4, 64, 2, 1
+#define MOE_DN_TILE 4, 4, 2, 2, 64, 2, 1
 #endif
 template <int WM_, int WN_, int MI_, int NI_, int BK_, int STAGES_, int OCC_>
 struct TileCfg {
@@ -42,8 +44,10 @@ using DownTile = TileCfg<MOE_DN_TILE>;
 static_assert(GateUpTile::BM == kBM && DownTile::BM == kBM, "row tiles of both GEMMs share the tile table");
 constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
 constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
-// FP8 GEMMs: 128 h columns (one 1 x 128 quantisation tile of h) per gate/up
-// tile, 256 output columns per down tile, K at most kFp8MaxKC chunks of 128.
+// FP8 GEMMs: 128 token rows; 128 h columns (one 1 x 128 quantisation tile of
+// h) per gate/up tile, 256 output columns per down tile, K at most kFp8MaxKC
+// chunks of 128.
+constexpr int kFp8BM = 128;
 constexpr int kFp8BNH = 128;
 constexpr int kFp8BN2 = 256;
 constexpr int kFp8MaxKC = 64;
@@ -61,6 +65,7 @@ struct TileDesc {
 };
 
 struct FfnLayout {
+  int bm;                        // token rows per tile
   int64_t R, Rs;                 // routed row-tile bound, shared row tiles
   int64_t nt1, nt1s, nt2;        // column tiles: gate/up routed, gate/up shared, down
   int64_t max1, max2;            // tile-table capacities
@@ -69,9 +74,10 @@ struct FfnLayout {
 
   explicit FfnLayout(const moe_cfg* c) {
     const int64_t P = pairs(c);
-    R = P / kBM + c->E;
-    Rs = c->S > 0 ? (c->T + kBM - 1) / kBM : 0;
     const bool f8 = c->wgt == MOE_FP8_E4M3;
+    bm = f8 ? kFp8BM : kBM;
+    R = P / bm + c->E;
+    Rs = c->S > 0 ? (c->T + bm - 1) / bm : 0;
     const int bnh = f8 ? kFp8BNH : kBNH, bn2 = f8 ? kFp8BN2 : kBN2;
     nt1 = (c->I + bnh - 1) / bnh;
     nt1s = ((int64_t)c->S * c->I + bnh - 1) / bnh;

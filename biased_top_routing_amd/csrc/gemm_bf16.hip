@@ -8,17 +8,17 @@
 // with fp32 accumulation (qwbw.cn essay, FP8 part of the infrastructure section,
 // keeps MoE gating in BF16/FP32).
 //
-// Tiling: a 256-thread workgroup computes a (2*MI*32) x 256 tile with four
-// wavefronts in a 2 x 2 grid; each wavefront owns MI x 4 MFMA 32x32 blocks.  A
-// and B K-slices of BK columns are staged through LDS (double-buffered, one
-// barrier per K step) with an XOR swizzle of the 16-byte chunks so that the
-// MFMA operand reads (32 rows x 16 bytes per half wave) hit distinct banks.
-// For gate/up, the tile's 256 weight rows are 128 gate rows and the 128 up rows
-// of the same intermediate columns, so SwiGLU is applied in registers.
+// Tiling: a workgroup of WM x WN wavefronts computes a (WM*MI*32) x (WN*NI*32)
+// tile; each wavefront owns MI x NI MFMA 32x32 blocks.  A and B K-slices of BK
+// columns are staged through LDS by direct-to-LDS buffer loads (a ring of
+// STAGES slices, one barrier per slice) with an XOR swizzle of the 16-byte
+// chunks so that the MFMA operand reads (32 rows x 16 bytes per half wave) hit
+// distinct banks.  For gate/up, the tile's weight rows are BN/2 gate rows and
+// the BN/2 up rows of the same intermediate columns, each wavefront holding
+// matching gate and up blocks, so SwiGLU is applied in registers.
 // Grouped tiles come from a device-built table (segment, first row, rows,
-// column tile) ordered column-tile-major inside a segment; the table is cut
-// into 8 contiguous ranges, one per XCD (workgroup id mod 8), so tiles sharing
-// a weight panel run together in one XCD's L2.
+// column tile); the table is cut into 8 contiguous ranges, one per XCD
+// (workgroup id mod 8), so tiles sharing operands run together in one XCD's L2.
 #include "common.h"
 #include "ffn_layout.h"
 #include "kernels.h"
@@ -93,16 +93,18 @@ __device__ __forceinline__ void wait_slices(int n) {
 // MI x NI MFMA 32x32 blocks.  K advances BK columns per slice through a ring of
 // STAGES LDS stages filled by direct-to-LDS loads.
 template <int MODE, int WM, int WN, int MI, int NI, int BK, int STAGES, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmParams p) {
-  static_assert(WM * WN == 4, "four wavefronts per workgroup");
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams p) {
+  constexpr int NW = WM * WN;             // wavefronts per workgroup
+  constexpr int NT = 64 * NW;             // threads
+  static_assert(NW == 4 || NW == 8 || NW == 16, "4, 8 or 16 wavefronts per workgroup");
   constexpr int BM = WM * MI * 32;
   constexpr int BN = WN * NI * 32;
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
-  constexpr int A_CH = BM * CPR / 256;    // direct-to-LDS loads per thread per slice
-  constexpr int B_CH = BN * CPR / 256;
+  constexpr int A_CH = BM * CPR / NT;     // direct-to-LDS loads per thread per slice
+  constexpr int B_CH = BN * CPR / NT;
   constexpr int PER = A_CH + B_CH;
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
-  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "whole loads per thread");
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
   static_assert(MODE != kGateUp || BN / 2 == kBNH, "gate/up tile width");
   static_assert(MODE != kDown || BN == kBN2, "down tile width");
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
@@ -165,20 +167,22 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmParams p) {
     ncols = p.H;
   }
 
-  // Direct-to-LDS loads: one global_load_lds_dwordx4 fills 1 KB of LDS, lane l
-  // at +16*l.  Instruction i of wave w covers chunks [(i*4 + w)*64, +64) of the
-  // A (or B) region; the lane loads the logical chunk that the XOR swizzle
-  // places at its physical position.  Rows past the valid range are clamped
-  // (their results are never stored).
+  // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds fills 1 KB of LDS,
+  // lane l at +16*l.  Instruction i of wave w covers chunks [(i*NW + w)*64, +64)
+  // of the A (or B) region; the lane loads the logical chunk that the XOR
+  // swizzle places at its physical position.  Token rows past the tile's valid
+  // rows get an offset outside the A descriptor, so the hardware drops them
+  // without a memory request (their LDS rows feed only outputs that are never
+  // stored); weight rows past the valid columns are clamped.
   int a_off[A_CH], b_off[B_CH];
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
-    const int q = (i * 4 + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
-    a_off[i] = min(r, rows - 1) * lda + swz<CPR>(r, pc) * 8;
+    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
+    a_off[i] = (r < rows ? r : rows + 1) * lda + swz<CPR>(r, pc) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
-    const int q = (i * 4 + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
+    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int wrow;
     if constexpr (MODE == kGateUp) {
       // rows [0, BN/2) gate, [BN/2, BN) up, of h columns nt*BN/2 + j
@@ -211,11 +215,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_bf16_kernel(GemmParams p) {
     const int wk = MODE == kDown ? (int)((k0v / p.I) * seg_kstride) + (k0v % p.I) : k0v;             \
     bf16_t* sb = lds + (stage_) * STAGE;                                                             \
     _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                 \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sb + (i * 4 + wave) * 512), 16, \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sb + (i * NW + wave) * 512), 16, \
                                                  a_off[i], k0v * 2, 0, 0);                           \
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w,                                             \
-                                                 (lds_void_t*)(sb + BM * BK + (i * 4 + wave) * 512), \
+                                                 (lds_void_t*)(sb + BM * BK + (i * NW + wave) * 512), \
                                                  16, b_off[i], wk * 2, 0, 0);                        \
   }
 
@@ -374,7 +378,8 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid),
+                         dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -388,7 +393,8 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max2, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DN_TILE>), dim3((unsigned)grid), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DN_TILE>), dim3((unsigned)grid),
+                         dim3(64 * DownTile::WM * DownTile::WN), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }

@@ -45,7 +45,7 @@ constexpr int kACh = kTM * kCPR / kThreads;   // direct-to-LDS loads per thread 
 constexpr int kBCh = kTN * kCPR / kThreads;
 constexpr int kPer = kACh + kBCh;
 constexpr int kStage = (kTM + kTN) * kBK;     // bytes per LDS stage
-static_assert(kTM == kBM, "row tiles shared with the tile table");
+static_assert(kTM == kFp8BM, "row tiles of the tile table");
 static_assert(kTN / 2 == kFp8BNH && kTN == kFp8BN2, "column tiles of the fp8 tile tables");
 
 struct Fp8Params {
@@ -172,7 +172,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
 #pragma unroll
   for (int i = 0; i < kACh; ++i) {
     const int q = (i * (kThreads / 64) + wave) * 64 + lane, r = q / kCPR, pc = q % kCPR;
-    a_off[i] = min(r, rows - 1) * lda + swz8(r, pc) * 16;
+    // rows past the valid ones: offset outside the A descriptor (dropped, no request)
+    a_off[i] = (r < rows ? r : rows + 1) * lda + swz8(r, pc) * 16;
   }
 #pragma unroll
   for (int i = 0; i < kBCh; ++i) {
