@@ -12,6 +12,45 @@ namespace moe {
 
 // One wavefront per token; 16-byte chunks (8 bf16 or 4 fp32 values) per lane.
 // y = y_shared + sum_j w_j * y_perm[inv_j], fp32 accumulation, j ascending.
+// The k routed rows of a chunk are loaded in batches of 8 before they are
+// accumulated, so that a lane keeps up to 9 loads in flight.  Each output row
+// is read once and written once: the loads and stores are non-temporal.
+#ifndef MOE_COMBINE_NT
+#define MOE_COMBINE_NT 1
+#endif
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+#if MOE_COMBINE_NT
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+#if MOE_COMBINE_NT
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+#else
+  *p = v;
+#endif
+}
+
+template <bool BF16>
+__device__ __forceinline__ void accum_chunk(float* acc, uint4 r, float g) {
+  const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      acc[2 * i] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] & 0xFFFF)), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] >> 16)), acc[2 * i + 1]);
+    } else {
+      acc[i] = fmaf(g, __uint_as_float(w4[i]), acc[i]);
+    }
+  }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y_perm,
                                                       const uint4* __restrict__ y_shared,
@@ -19,6 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const float* __restrict__ topk_w, int T,
                                                       int k, int64_t nchunk,
                                                       uint4* __restrict__ y) {
+  constexpr int KB = 8;   // routed rows loaded per batch
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -27,35 +67,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
   constexpr int V = BF16 ? 8 : 4;
   for (int64_t c = lane; c < nchunk; c += kWave) {
     float acc[V];
-    if (y_shared) {
-      const uint4 r = y_shared[t * nchunk + c];
-      const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (BF16) {
-          acc[2 * i] = bf16_to_f32((bf16_t)(w4[i] & 0xFFFF));
-          acc[2 * i + 1] = bf16_to_f32((bf16_t)(w4[i] >> 16));
-        } else {
-          acc[i] = __uint_as_float(w4[i]);
-        }
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    if (y_shared) accum_chunk<BF16>(acc, ld_stream(&y_shared[t * nchunk + c]), 1.0f);
+    for (int j0 = 0; j0 < k; j0 += KB) {
+      uint4 r[KB];
+#pragma unroll
+      for (int jj = 0; jj < KB; ++jj) {
+        // slots past k reload slot j0's row (kept in range, weight 0 below)
+        const int j = j0 + jj < k ? j0 + jj : j0;
+        const int64_t p = __shfl(myp, j);
+        r[jj] = ld_stream(&y_perm[p * nchunk + c]);
       }
-    } else {
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    }
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = __shfl(myp, j);
-      const float g = __shfl(myw, j);
-      const uint4 r = y_perm[p * nchunk + c];
-      const uint32_t w4[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (BF16) {
-          acc[2 * i] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] & 0xFFFF)), acc[2 * i]);
-          acc[2 * i + 1] = fmaf(g, bf16_to_f32((bf16_t)(w4[i] >> 16)), acc[2 * i + 1]);
-        } else {
-          acc[i] = fmaf(g, __uint_as_float(w4[i]), acc[i]);
-        }
+      for (int jj = 0; jj < KB; ++jj) {
+        const int j = j0 + jj < k ? j0 + jj : j0;
+        const float g = __shfl(myw, j);
+        if (j0 + jj < k) accum_chunk<BF16>(acc, r[jj], g);
       }
     }
     uint4 o;
@@ -66,7 +94,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
       o = make_uint4(__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
                      __float_as_uint(acc[3]));
     }
-    y[t * nchunk + c] = o;
+    st_stream(&y[t * nchunk + c], o);
   }
 }
 

@@ -136,7 +136,21 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
 }
 
 // One wavefront per token: load the token's row once, store it to each of its
-// k destination rows.  16-byte chunks; CPL chunks per lane per pass.
+// k destination rows.  16-byte chunks; CPL chunks per lane per pass.  The
+// permuted rows are written once and read later by another kernel: the
+// stores are non-temporal.
+#ifndef MOE_PERMUTE_NT
+#define MOE_PERMUTE_NT 1
+#endif
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void st_stream(uint4* p, uint4 v) {
+#if MOE_PERMUTE_NT
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+#else
+  *p = v;
+#endif
+}
 template <int CPL>
 __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restrict__ src,
                                                            const int32_t* __restrict__ inv, int T,
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restri
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int64_t c = c0 + i * kWave + lane;
-        if (c < nchunk) dst[p * nchunk + c] = v[i];
+        if (c < nchunk) st_stream(&dst[p * nchunk + c], v[i]);
       }
     }
   }
