@@ -236,6 +236,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   const int lr = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) a_rd[mi] = wm * MI * 32 + mi * 32 + lr;
+  // A wavefront whose token rows all lie past the tile's valid rows skips its
+  // operand reads and MFMAs (one wave-uniform branch per slice: a small tile,
+  // e.g. at decode size, then costs little more than its loads).
+  const bool has_rows = wm * MI * 32 < rows;
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     int brow;
@@ -269,6 +273,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     // Operand fragments are double-buffered across the BK/16 MFMA k-steps: the
     // reads of step kk+1 are interleaved with the MFMAs of step kk.
     constexpr int KK = BK / 16;
+    if (has_rows) {
     bf16x8_t fa[2][MI], fb[2][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -298,6 +303,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc[mi][ni], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    }   // has_rows
     cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
 #undef MOE_ISSUE
