@@ -44,6 +44,26 @@ using DownTile = TileCfg<MOE_DN_TILE>;
 static_assert(GateUpTile::BM == kBM && DownTile::BM == kBM, "row tiles of both GEMMs share the tile table");
 constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
 constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
+// Small batches (at most kDecBM routed rows per expert on average, e.g. decode):
+// the GEMMs only stream weights, so their tiles are 32 token rows x 256 weight
+// rows with a deeper ring (more weight bytes in flight per CU).
+#ifndef MOE_DEC_GU_TILE
+#define MOE_DEC_GU_TILE 1, 4, 1, 2, 64, 4, 1
+#endif
+#ifndef MOE_DEC_DN_TILE
+#define MOE_DEC_DN_TILE 1, 4, 1, 2, 64, 4, 1
+#endif
+using DecGateUpTile = TileCfg<MOE_DEC_GU_TILE>;
+using DecDownTile = TileCfg<MOE_DEC_DN_TILE>;
+constexpr int kDecBM = 32;
+static_assert(DecGateUpTile::BM == kDecBM && DecDownTile::BM == kDecBM, "row tiles of the small-batch table");
+constexpr int kDecBNH = DecGateUpTile::BN / 2;
+constexpr int kDecBN2 = DecDownTile::BN;
+static_assert(kDecBNH == kBNH, "h column tiles of both bf16 configurations (I % 128 check)");
+
+inline bool small_batch(const moe_cfg* c) {
+  return c->act == MOE_BF16 && c->wgt == MOE_BF16 && pairs(c) <= (int64_t)kDecBM * c->E;
+}
 // FP8 GEMMs: 128 token rows; 128 h columns (one 1 x 128 quantisation tile of
 // h) per gate/up tile, 256 output columns per down tile, K at most kFp8MaxKC
 // chunks of 128.
@@ -65,6 +85,7 @@ struct TileDesc {
 };
 
 struct FfnLayout {
+  bool dec;                      // small-batch bf16 configuration
   int bm;                        // token rows per tile
   int64_t R, Rs;                 // routed row-tile bound, shared row tiles
   int64_t nt1, nt1s, nt2;        // column tiles: gate/up routed, gate/up shared, down
@@ -75,10 +96,11 @@ struct FfnLayout {
   explicit FfnLayout(const moe_cfg* c) {
     const int64_t P = pairs(c);
     const bool f8 = c->wgt == MOE_FP8_E4M3;
-    bm = f8 ? kFp8BM : kBM;
+    dec = small_batch(c);
+    bm = f8 ? kFp8BM : dec ? kDecBM : kBM;
     R = P / bm + c->E;
     Rs = c->S > 0 ? (c->T + bm - 1) / bm : 0;
-    const int bnh = f8 ? kFp8BNH : kBNH, bn2 = f8 ? kFp8BN2 : kBN2;
+    const int bnh = f8 ? kFp8BNH : dec ? kDecBNH : kBNH, bn2 = f8 ? kFp8BN2 : dec ? kDecBN2 : kBN2;
     nt1 = (c->I + bnh - 1) / bnh;
     nt1s = ((int64_t)c->S * c->I + bnh - 1) / bnh;
     nt2 = (c->H + bn2 - 1) / bn2;

@@ -105,8 +105,6 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   constexpr int PER = A_CH + B_CH;
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
-  static_assert(MODE != kGateUp || BN / 2 == kBNH, "gate/up tile width");
-  static_assert(MODE != kDown || BN == kBN2, "down tile width");
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
   __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * STAGE];
 
@@ -384,8 +382,12 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid),
-                         dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
+      if (L.dec)
+        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_DEC_GU_TILE>), dim3((unsigned)grid),
+                           dim3(64 * DecGateUpTile::WM * DecGateUpTile::WN), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid),
+                           dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -399,8 +401,12 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
     const int64_t grid = align_up((size_t)L.max2, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DN_TILE>), dim3((unsigned)grid),
-                         dim3(64 * DownTile::WM * DownTile::WN), 0, st, p);
+      if (L.dec)
+        hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DEC_DN_TILE>), dim3((unsigned)grid),
+                           dim3(64 * DecDownTile::WM * DecDownTile::WN), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DN_TILE>), dim3((unsigned)grid),
+                           dim3(64 * DownTile::WM * DownTile::WN), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
