@@ -14,7 +14,8 @@ namespace moe {
 // ------------------------------------------------------------ tile tables
 // Segments 0..E-1 are the routed experts (rows offsets[e]..offsets[e+1] of the
 // permuted rows); segment E is the shared experts over all T tokens.  Each
-// segment contributes ceil(rows / bm) row tiles times its column tiles.
+// segment contributes ceil(rows / bm) row tiles times its column tiles, with
+// the row height bm of the GEMM the table is for.
 // Inside a segment the row tiles are cut into groups of kGroupRowTiles; a
 // group's tiles are listed column-tile-major.  Tiles that run at the same time
 // on one XCD (consecutive entries) then cover a few row tiles times a few
@@ -22,21 +23,23 @@ namespace moe {
 // shared in that XCD's L2, also for segments far larger than the number of
 // tiles in flight.  One workgroup; exclusive prefix sums over segments in LDS.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int S, int T, int bm, int nt1, int nt1s, int nt2,
+                                                           int S, int T, int bm1, int bm2, int nt1, int nt1s,
+                                                           int nt2,
                                                            TileDesc* __restrict__ t1,
                                                            TileDesc* __restrict__ t2,
                                                            int32_t* __restrict__ hdr) {
-  __shared__ int32_t pre1[1024], pre2[1024], mt_s[1024], row0_s[1024], rows_s[1024];
+  __shared__ int32_t pre1[1024], pre2[1024], mt1_s[1024], mt2_s[1024], row0_s[1024], rows_s[1024];
   const int tid = threadIdx.x;
   const int nseg = E + (S > 0 ? 1 : 0);
   int c1 = 0, c2 = 0;
   if (tid < nseg) {
     const int rows = tid < E ? offsets[tid + 1] - offsets[tid] : T;
     const int row0 = tid < E ? offsets[tid] : 0;
-    const int mt = (rows + bm - 1) / bm;
-    c1 = mt * (tid < E ? nt1 : nt1s);
-    c2 = mt * nt2;
-    mt_s[tid] = mt;
+    const int mt1 = (rows + bm1 - 1) / bm1, mt2 = (rows + bm2 - 1) / bm2;
+    c1 = mt1 * (tid < E ? nt1 : nt1s);
+    c2 = mt2 * nt2;
+    mt1_s[tid] = mt1;
+    mt2_s[tid] = mt2;
     row0_s[tid] = row0;
     rows_s[tid] = rows;
   }
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       // skip empty segments that share the same prefix value
       while (g + 1 < nseg && pre[g + 1] <= L) ++g;
       const int local = L - pre[g];
-      const int mt = mt_s[g];
+      const int mt = pass == 0 ? mt1_s[g] : mt2_s[g];
+      const int bm = pass == 0 ? bm1 : bm2;
       const int ncol = (pass == 0 ? (g < E ? nt1 : nt1s) : nt2);
       const int q = local / (kGroupRowTiles * ncol);             // row-tile group (all earlier ones full)
       const int idx = local - q * kGroupRowTiles * ncol;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm,
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm1, L.bm2,
                      (int)L.nt1, (int)L.nt1s, (int)L.nt2,
                      reinterpret_cast<TileDesc*>(base + L.off_t1),
                      reinterpret_cast<TileDesc*>(base + L.off_t2),

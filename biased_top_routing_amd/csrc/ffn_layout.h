@@ -18,18 +18,17 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 }
 
 // ---- expert FFN tiling shared by the tile-table builder and the GEMMs
-#ifndef MOE_TILE_BM
-#define MOE_TILE_BM 256
-#endif
-constexpr int kBM = MOE_TILE_BM;  // rows of a bf16 GEMM tile (tokens)
+
 // Tile shapes of the grouped GEMMs (compile-time choices):
 // WM, WN wavefronts along tokens / weights; MI, NI MFMA 32x32 blocks per
 // wavefront; BK K-depth of an LDS stage; STAGES ring depth; OCC workgroups
-// per CU the kernel is built for.  Both default to 256 x 256 tiles with two
-// or four wavefronts per SIMD (measured: a second wavefront per SIMD covers
-// the load and barrier waits that a single wavefront exposes).
+// per CU the kernel is built for.  Two or four wavefronts per SIMD (measured:
+// a second wavefront per SIMD covers the load and barrier waits that a single
+// wavefront exposes).  Gate/up tiles are 320 token rows high so that a
+// routed segment of up to 640 rows (balanced loads sit near T*k/E = 512 at the
+// V3-like shape) loads its weight panel twice, not three times.
 #ifndef MOE_GU_TILE
-#define MOE_GU_TILE 2, 4, 4, 2, 64, 2, 1
+#define MOE_GU_TILE 2, 4, 5, 2, 64, 2, 1
 #endif
 #ifndef MOE_DN_TILE
 #define MOE_DN_TILE 4, 4, 2, 2, 64, 2, 1
@@ -41,7 +40,8 @@ struct TileCfg {
 };
 using GateUpTile = TileCfg<MOE_GU_TILE>;
 using DownTile = TileCfg<MOE_DN_TILE>;
-static_assert(GateUpTile::BM == kBM && DownTile::BM == kBM, "row tiles of both GEMMs share the tile table");
+constexpr int kBM1 = GateUpTile::BM;      // token rows of a gate/up tile
+constexpr int kBM2 = DownTile::BM;        // token rows of a down tile
 constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
 constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
 // Small batches (at most kDecBM routed rows per expert on average, e.g. decode):
@@ -86,8 +86,8 @@ struct TileDesc {
 
 struct FfnLayout {
   bool dec;                      // small-batch bf16 configuration
-  int bm;                        // token rows per tile
-  int64_t R, Rs;                 // routed row-tile bound, shared row tiles
+  int bm1, bm2;                  // token rows per tile: gate/up, down
+  int64_t R1, Rs1, R2, Rs2;      // routed row-tile bounds, shared row tiles
   int64_t nt1, nt1s, nt2;        // column tiles: gate/up routed, gate/up shared, down
   int64_t max1, max2;            // tile-table capacities
   size_t off_hdr, off_t1, off_t2, off_hp, off_hps, off_hs, off_hss, off_xq, off_xqs, total;
@@ -97,15 +97,18 @@ struct FfnLayout {
     const int64_t P = pairs(c);
     const bool f8 = c->wgt == MOE_FP8_E4M3;
     dec = small_batch(c);
-    bm = f8 ? kFp8BM : dec ? kDecBM : kBM;
-    R = P / bm + c->E;
-    Rs = c->S > 0 ? (c->T + bm - 1) / bm : 0;
+    bm1 = f8 ? kFp8BM : dec ? kDecBM : kBM1;
+    bm2 = f8 ? kFp8BM : dec ? kDecBM : kBM2;
+    R1 = P / bm1 + c->E;
+    Rs1 = c->S > 0 ? (c->T + bm1 - 1) / bm1 : 0;
+    R2 = P / bm2 + c->E;
+    Rs2 = c->S > 0 ? (c->T + bm2 - 1) / bm2 : 0;
     const int bnh = f8 ? kFp8BNH : dec ? kDecBNH : kBNH, bn2 = f8 ? kFp8BN2 : dec ? kDecBN2 : kBN2;
     nt1 = (c->I + bnh - 1) / bnh;
     nt1s = ((int64_t)c->S * c->I + bnh - 1) / bnh;
     nt2 = (c->H + bn2 - 1) / bn2;
-    max1 = R * nt1 + Rs * nt1s;
-    max2 = (R + Rs) * nt2;
+    max1 = R1 * nt1 + Rs1 * nt1s;
+    max2 = (R2 + Rs2) * nt2;
     hbytes = c->wgt == MOE_FP8_E4M3 ? 1 : (int)act_bytes(c);
     const bool fp8 = c->wgt == MOE_FP8_E4M3;
     size_t o = 0;
