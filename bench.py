@@ -204,6 +204,66 @@ def decode_extra(layer, c, w, steps, warmup):
             "bytes": wbytes + iobytes, "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
 
 
+def balance_trajectory(layer, c, w, steps):
+    """Max/mean expert load over `steps` consecutive batches of the layer with the bias
+    update between them.  Each batch's x is drawn on the GPU (torch's generator seeded
+    with the step number, N(0,1), rounded to bf16): same distribution as the shared
+    generator, without minutes of host-side sampling."""
+    import torch
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    g = torch.Generator(device="cuda")
+    ratios = []
+    mean = c.T * c.k / c.E
+    for step in range(steps):
+        g.manual_seed(1000 + step)
+        x = torch.randn(c.T, c.H, device="cuda", generator=g).to(torch.bfloat16)
+        layer.forward(x, bias, gamma=c.gamma)
+        ratios.append(float(layer.counts.max().item()) / mean)
+    pick = [1, 10, 25, 50, 100]
+    return {"steps": steps, "max_over_mean_at_step": {str(i): round(ratios[i - 1], 3) for i in pick if i <= steps},
+            "min_over_steps": round(min(ratios), 3), "x": "N(0,1) drawn on the GPU per step, seeded"}
+
+
+def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
+    """The route stage alone (router GEMM + sigmoid + biased group-limited top-k) and the
+    top-k kernel alone (scores given) at several batch sizes, with a 512 MB write
+    between launches so that no input is served from the 256 MB Infinity Cache."""
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    out = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    wr = to_dev(w.w_router)
+    off = torch.from_numpy(w.logit_offset).cuda() if w.logit_offset is not None else None
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    for T in sizes:
+        cfg = L.cfg_from(c, T=T)
+        x = torch.randn(T, c.H, device="cuda").to(torch.bfloat16)
+        scores = torch.empty(T, c.E, device="cuda")
+        idx = torch.empty(T, c.k, dtype=torch.int32, device="cuda")
+        gw = torch.empty(T, c.k, device="cuda")
+        res = {}
+        for name, flags in (("route", 0), ("topk", L.MOE_SCORES_IN)):
+            L.moe_route(cfg, x, wr, off, bias, scores, flags, idx, gw)
+            ms = []
+            for _ in range(iters):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                L.moe_route(cfg, x, wr, off, bias, scores, flags, idx, gw)
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            t = sorted(ms)[len(ms) // 2]
+            nbytes = (T * c.H * 2 + c.E * c.H * 2 + T * c.E * 4 if flags == 0 else T * c.E * 4) + c.E * 4 + T * c.k * 8
+            res[name] = {"ms": round(t, 4), "gbs": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes}
+        out[str(T)] = res
+        del x, scores, idx, gw
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def gemm_summary(c, ms_per_step, stage_ms):
     peak = PEAK_FP8_TFLOPS if c.wgt == "fp8_e4m3" else PEAK_BF16_TFLOPS
     gu = c.gate_up_flops() / (stage_ms["gate_up"] * 1e-3) / 1e12
@@ -305,6 +365,8 @@ def main():
         extras = {}
         log("extra: the same layer at decode size")
         extras["v3_decode_bf16"] = decode_extra(layer, c, w, max(args.steps, 20), args.warmup)
+        log("extra: route stage at several batch sizes (cache flushed between launches)")
+        extras["route_sweep"] = route_sweep(c, w)
         del layer, x
         torch.cuda.empty_cache()
         cf = CONFIGS["v3_fp8"]
@@ -324,6 +386,8 @@ def main():
                                                   (msf * 1e-3) / 1e12, 2),
                             "max_over_mean_load": round(float(cnt.max() / (cf.T * cf.k / cf.E)), 3),
                             "stages_ms": {k: round(v, 4) for k, v in stf.items()}}
+        log("extra: FP8 layer, 100 batches with the bias update between them")
+        extras["v3_fp8"]["balance"] = balance_trajectory(lf, cf, wf, cf.steps)
         del lf, xf
         torch.cuda.empty_cache()
         out["other_workloads"] = extras

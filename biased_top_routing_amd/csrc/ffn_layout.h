@@ -33,6 +33,10 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 #ifndef MOE_DN_TILE
 #define MOE_DN_TILE 4, 4, 2, 2, 64, 2, 1
 #endif
+// Router GEMM tile (tokens x experts): 64 x 256, 8 wavefronts, 3-slice ring
+#ifndef MOE_RT_TILE
+#define MOE_RT_TILE 2, 4, 1, 2, 64, 3, 1
+#endif
 template <int WM_, int WN_, int MI_, int NI_, int BK_, int STAGES_, int OCC_>
 struct TileCfg {
   static constexpr int WM = WM_, WN = WN_, MI = MI_, NI = NI_, BK = BK_, STAGES = STAGES_, OCC = OCC_;

@@ -357,8 +357,9 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   p.offset = offset;
   p.out_routed = scores;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-  const dim3 grid((unsigned)((c->T + 63) / 64), (unsigned)((c->E + 255) / 256));
-  hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, 2, 2, 1, 4, 64, 3, 1>), grid, dim3(256), 0, st, p);
+  using RT = TileCfg<MOE_RT_TILE>;
+  const dim3 grid((unsigned)((c->T + RT::BM - 1) / RT::BM), (unsigned)((c->E + RT::BN - 1) / RT::BN));
+  hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, MOE_RT_TILE>), grid, dim3(64 * RT::WM * RT::WN), 0, st, p);
   return launch_status();
 }
 

@@ -153,6 +153,195 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
+// Fast form for E = 16 * EPL with groups of whole lanes: one token per 16
+// lanes (four per wavefront), lane l of a slice holds experts [l*EPL, (l+1)*EPL)
+// in registers and every group spans LG = (E/G)/EPL consecutive lanes (a power
+// of two).  No LDS and no barrier:
+//   each lane keeps the top-TOPR biased scores of its experts; the LG lanes of
+//   a group merge their lists with xor shuffles, so each holds the group's
+//   top-TOPR and adds them largest first (fp32), as the reference does;
+//   a group's rank = number of groups with a larger score or an equal score
+//   and a lower index (group scores gathered by shuffles); chosen = rank < M;
+//   k rounds of a 16-lane max over 64-bit keys (order key of q, ~expert), the
+//   affinity s of the round's winner travelling with its key.
+// Cross-lane moves inside a row of 16 lanes with DPP (VALU rate, no LDS):
+// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at xor 1 and xor 2; the
+// half-row mirror pairs lane i with 7-i and the row mirror lane i with 15-i.
+// Applied in this order, each step pairs lanes whose partial results cover
+// disjoint lane sets, so after 1/2/3/4 steps every lane holds the result over
+// its 2/4/8/16-lane block.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// One step of the (64-bit key, value) max: keep the larger key and its value.
+template <int CTRL>
+__device__ __forceinline__ void max_step(uint64_t& best, float& val) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)best);
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(best >> 32));
+  const float ov = dpp_f32<CTRL>(val);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  const bool gt = o > best;
+  best = gt ? o : best;
+  val = gt ? ov : val;
+}
+
+// Merge the partner's top-R list into this lane's (both descending).
+template <int CTRL, int R>
+__device__ __forceinline__ void merge_step(float (&top)[R]) {
+  float other[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) other[i] = dpp_f32<CTRL>(top[i]);
+#pragma unroll
+  for (int i2 = 0; i2 < R; ++i2) {
+    float v = other[i2];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float hi = fmaxf(top[i], v), lo = fminf(top[i], v);
+      top[i] = hi;
+      v = lo;
+    }
+  }
+}
+
+template <int EPL, int TOPR>
+__global__ __launch_bounds__(256) void route_topk16_kernel(
+    const float* __restrict__ scores, const float* __restrict__ bias, int T, int E, int G, int M,
+    int k, float scale, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  constexpr int LPT = 16;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int sl = lane & (LPT - 1);
+  const int slice0 = lane & ~(LPT - 1);                   // first lane of this token's slice
+  const int LG = (E / G) / EPL;                           // lanes per group
+  const int grp = sl / LG;
+  float b[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) b[j] = bias[sl * EPL + j];
+  const int64_t tokens_per_grid = (int64_t)gridDim.x * (blockDim.x / LPT);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / LPT) + (threadIdx.x / LPT); t - (threadIdx.x % kWave) / LPT <
+       (int64_t)T; t += tokens_per_grid) {
+    // (the loop condition keeps whole wavefronts iterating together; lanes of a
+    //  token past T load nothing and store nothing)
+    const bool valid = t < T;
+    float s[EPL], q[EPL];
+    const float* row = scores + (valid ? t : 0) * E + sl * EPL;
+    if constexpr (EPL % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < EPL; j += 4) {
+        const float4 v = valid ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) s[j] = valid ? row[j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) q[j] = s[j] + b[j];
+    // ---- group score: top-TOPR of the group, summed largest first
+    float top[TOPR];
+#pragma unroll
+    for (int i = 0; i < TOPR; ++i) top[i] = -__builtin_huge_valf();
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      float v = q[j];
+#pragma unroll
+      for (int i = 0; i < TOPR; ++i) {
+        const float hi = fmaxf(top[i], v), lo = fminf(top[i], v);
+        top[i] = hi;
+        v = lo;
+      }
+    }
+    // the LG lanes of a group (an aligned block of 1, 2, 4, 8 or 16 lanes)
+    if (LG >= 2) merge_step<kDppXor1>(top);
+    if (LG >= 4) merge_step<kDppXor2>(top);
+    if (LG >= 8) merge_step<kDppHalfMirror>(top);
+    if (LG >= 16) merge_step<kDppMirror>(top);
+    float gs = top[0];
+#pragma unroll
+    for (int i = 1; i < TOPR; ++i) gs = gs + top[i];
+    // ---- group rank among the G groups of this token
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const float o = __shfl(gs, slice0 + h * LG);
+      rank += (o > gs) || (o == gs && h < grp);
+    }
+    const bool chosen = rank < M;
+    // ---- k rounds of the 16-lane max
+    uint64_t key[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const uint32_t e = (uint32_t)(sl * EPL + j);
+      key[j] = (valid && chosen) ? (((uint64_t)float_order_key(q[j]) << 32) | (uint64_t)(0xFFFFFFFFu - e)) : 0ull;
+    }
+    int my_e = 0;
+    float my_s = 0.f;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = key[0];
+      float bs = s[0];
+#pragma unroll
+      for (int j = 1; j < EPL; ++j) {
+        const bool gt = key[j] > best;
+        best = gt ? key[j] : best;
+        bs = gt ? s[j] : bs;
+      }
+      max_step<kDppXor1>(best, bs);
+      max_step<kDppXor2>(best, bs);
+      max_step<kDppHalfMirror>(best, bs);
+      max_step<kDppMirror>(best, bs);
+      if (sl == r) {
+        my_e = (int)(0xFFFFFFFFu - (uint32_t)best);
+        my_s = bs;
+      }
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) key[j] = key[j] == best ? 0ull : key[j];
+    }
+    float tot = sl < k ? my_s : 0.f;
+    tot += dpp_f32<kDppXor1>(tot);
+    tot += dpp_f32<kDppXor2>(tot);
+    tot += dpp_f32<kDppHalfMirror>(tot);
+    tot += dpp_f32<kDppMirror>(tot);
+    if (valid && sl < k) {
+      idx_out[t * k + sl] = my_e;
+      w_out[t * k + sl] = scale * my_s / tot;
+    }
+  }
+}
+
+// E = 16 * EPL, groups of whole lanes (LG a power of two), k <= 16, top-r <= 4.
+static bool topk16_fits(const moe_cfg* c) {
+  if (c->E % 16 || c->E / 16 > 16 || c->k > 16 || c->group_topr > 4) return false;
+  const int epl = c->E / 16, gsz = c->E / c->G;
+  if (gsz % epl) return false;
+  const int lg = gsz / epl;
+  return (lg & (lg - 1)) == 0;
+}
+
+template <int EPL, int TOPR>
+static void launch_topk16(const moe_cfg* c, const float* scores, const float* bias, int32_t* idx,
+                          float* w, hipStream_t st) {
+  const int blocks = (int)std::min<int64_t>(((int64_t)c->T + 15) / 16, 16384);
+  hipLaunchKernelGGL((route_topk16_kernel<EPL, TOPR>), dim3(blocks), dim3(256), 0, st, scores, bias, c->T,
+                     c->E, c->G, c->M, c->k, c->route_scale, idx, w);
+}
+
+template <int EPL>
+static void launch_topk16_r(const moe_cfg* c, const float* scores, const float* bias, int32_t* idx,
+                            float* w, hipStream_t st) {
+  switch (c->group_topr) {
+    case 1: launch_topk16<EPL, 1>(c, scores, bias, idx, w, st); break;
+    case 2: launch_topk16<EPL, 2>(c, scores, bias, idx, w, st); break;
+    case 3: launch_topk16<EPL, 3>(c, scores, bias, idx, w, st); break;
+    default: launch_topk16<EPL, 4>(c, scores, bias, idx, w, st); break;
+  }
+}
+
 template <int EPL, int LPT>
 static void launch_topk(const moe_cfg* c, const float* scores, const float* bias, int32_t* idx,
                         float* w, hipStream_t st) {
@@ -165,6 +354,18 @@ static void launch_topk(const moe_cfg* c, const float* scores, const float* bias
 
 moe_status launch_route_topk(const moe_cfg* c, const float* scores, const float* bias, int32_t* idx,
                              float* w, hipStream_t st) {
+  if (topk16_fits(c)) {
+    switch (c->E / 16) {
+      case 1: launch_topk16_r<1>(c, scores, bias, idx, w, st); break;
+      case 2: launch_topk16_r<2>(c, scores, bias, idx, w, st); break;
+      case 4: launch_topk16_r<4>(c, scores, bias, idx, w, st); break;
+      case 8: launch_topk16_r<8>(c, scores, bias, idx, w, st); break;
+      case 16: launch_topk16_r<16>(c, scores, bias, idx, w, st); break;
+      default: goto general;
+    }
+    return launch_status();
+  }
+general:
   if (c->E <= 16) launch_topk<1, 16>(c, scores, bias, idx, w, st);
   else if (c->E <= 32) launch_topk<1, 32>(c, scores, bias, idx, w, st);
   else if (c->E <= 64) launch_topk<1, 64>(c, scores, bias, idx, w, st);

@@ -39,6 +39,13 @@ ROUTE_CASES = [
     (96, 12, 5, 7, 4, 300, "ties"),
     (8, 1, 1, 8, 2, 100, "uniform"),
     (32, 32, 32, 32, 1, 100, "ties"),
+    # the 16-lane form: one, two, four and eight lanes per group, top-r up to 4
+    (128, 16, 4, 8, 3, 777, "uniform"),
+    (256, 8, 4, 8, 4, 513, "ties"),
+    (256, 4, 2, 8, 1, 400, "uniform"),
+    (32, 2, 1, 4, 2, 333, "ties"),
+    (256, 16, 4, 16, 2, 300, "zeros"),
+    (64, 8, 3, 6, 2, 1, "uniform"),
 ]
 
 

@@ -182,3 +182,34 @@ def test_layer_mid_bf16_balance_loop():
         bias_h = bias_next
     say(f"  max/mean load first {ratios[0]:.2f} last {ratios[-1]:.2f}")
     assert ratios[-1] < ratios[0]
+
+
+def test_layer_determinism_and_routing_invariants():
+    """Two runs of the same batch give bitwise-equal routing, dispatch, bias and
+    layer output; on the GPU's own outputs every token uses at most M groups and
+    its gates sum to the gate scale (to k ulps), and gates recomputed from the
+    GPU's fp32 affinities equal the GPU's gates (the bias never enters them)."""
+    c = MID.with_(T=2048)
+    wts = make_weights(c)
+    layer = MoeLayerGPU(c, wts)
+    xh = make_x(c, 0)
+    outs = []
+    for run in range(2):
+        say(f"mid bf16 determinism run {run}")
+        bias = dev_f32(wts.bias0)
+        y = layer.forward(to_device(xh), bias, gamma=c.gamma)
+        torch.cuda.synchronize()
+        outs.append({n: host(getattr(layer, n)).copy() for n in ("topk_idx", "topk_w", "counts", "offsets",
+                                                                   "perm", "inv", "scores")})
+        outs[-1]["y"] = host(y).copy()
+        outs[-1]["bias"] = host(bias).copy()
+    for n in outs[0]:
+        a, b = outs[0][n], outs[1][n]
+        assert a.dtype == b.dtype and (a.view(np.uint8) == b.view(np.uint8)).all(), n
+    idx, w, s = outs[0]["topk_idx"], outs[0]["topk_w"], outs[0]["scores"]
+    groups = idx // (c.E // c.G)
+    assert max(len(set(r)) for r in groups) <= c.M
+    ulp = np.spacing(np.float32(c.route_scale))
+    assert np.abs(w.astype(np.float64).sum(1) - c.route_scale).max() <= c.k * ulp
+    sel = np.take_along_axis(s.astype(np.float64), idx.astype(np.int64), 1)
+    np.testing.assert_allclose(w, c.route_scale * sel / sel.sum(1, keepdims=True), rtol=2e-6, atol=0)
