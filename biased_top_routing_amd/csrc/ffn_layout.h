@@ -68,10 +68,10 @@ static_assert(kDecBNH == kBNH, "h column tiles of both bf16 configurations (I % 
 inline bool small_batch(const moe_cfg* c) {
   return c->act == MOE_BF16 && c->wgt == MOE_BF16 && pairs(c) <= (int64_t)kDecBM * c->E;
 }
-// FP8 GEMMs: 128 token rows; 128 h columns (one 1 x 128 quantisation tile of
+// FP8 GEMMs: 256 token rows; 128 h columns (one 1 x 128 quantisation tile of
 // h) per gate/up tile, 256 output columns per down tile, K at most kFp8MaxKC
 // chunks of 128.
-constexpr int kFp8BM = 128;
+constexpr int kFp8BM = 256;
 constexpr int kFp8BNH = 128;
 constexpr int kFp8BN2 = 256;
 constexpr int kFp8MaxKC = 64;

@@ -8,19 +8,25 @@
 // On gfx950 one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K
 // chunk, so the promotion is: P = A_c B_c^T of the chunk from a zero
 // accumulator, then acc += P * sa[row, c] * sw[block, c] in fp32 registers.
+// (The FP8 MFMA's own sum of a chunk's products is not exact for codes of a
+// wide exponent range; starting every chunk from zero keeps that error from
+// growing with K.)
 //   gate/up  h = silu(X W_g^T) * (X W_u^T), quantised per 1 x 128 tile of h in
 //            the epilogue (codes + one fp32 scale per tile)
 //   down     Y = h W_d^T, stored as bf16
 //
-// Tiling: a 512-thread workgroup (8 wavefronts, 2 x 4) computes a 128 x 256
-// tile; each wavefront owns 4 x 4 MFMA 16 x 16 blocks (64 x 64).  K advances
-// 128 bytes per slice through a ring of LDS stages filled by direct-to-LDS
-// buffer loads (16-byte chunks, XOR swizzle per row).  The tile's activation
-// scales (all K chunks) and weight scales are staged in LDS once per tile.
-// The gate/up tile's 256 weight rows are the 128 gate rows and the 128 up rows
-// of 128 h columns, so SwiGLU and the 1 x 128 quantisation of h stay inside
-// the workgroup.  Tile tables and the XCD-aware ordering are those of the bf16
-// GEMMs.
+// Tiling: a workgroup of WM x WN wavefronts computes a (WM*MI*16) x (WN*NI*16)
+// tile; each wavefront owns MI x NI MFMA 16 x 16 blocks.  K advances 128 bytes
+// per slice through a ring of LDS stages filled by direct-to-LDS buffer loads
+// (16-byte chunks, XOR swizzle per row); the tile's activation scales of the
+// slice ride in the same stage (one 4-byte load per lane; wavefronts without
+// scale rows issue an equal load that the range check drops, so every
+// wavefront waits on the same count).  Weight-block scales of all chunks are
+// staged once per tile.  The gate/up tile's 256 weight rows are the 128 gate
+// rows and the 128 up rows of 128 h columns, so SwiGLU and the 1 x 128
+// quantisation of h stay inside the workgroup.  All LDS is one array: with
+// several LDS objects the compiler makes every LDS read wait for the
+// direct-to-LDS loads in flight.
 #include "common.h"
 #include "ffn_layout.h"
 #include "kernels.h"
@@ -28,25 +34,17 @@
 namespace moe {
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4v_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
 enum { kGateUp8 = 1, kDown8 = 2 };
 
-constexpr int kWM = 2, kWN = 4;           // wavefront grid
-constexpr int kMI = 4, kNI = 4;           // 16 x 16 blocks per wavefront
-constexpr int kTM = kWM * kMI * 16;       // 128 token rows
-constexpr int kTN = kWN * kNI * 16;       // 256 weight rows
-constexpr int kBK = 128;                  // K bytes per slice = one scale chunk
-constexpr int kCPR = kBK / 16;            // 16-byte chunks per LDS row
-constexpr int kThreads = kWM * kWN * 64;  // 512
-constexpr int kACh = kTM * kCPR / kThreads;   // direct-to-LDS loads per thread per slice
-constexpr int kBCh = kTN * kCPR / kThreads;
-constexpr int kPer = kACh + kBCh;
-constexpr int kStage = (kTM + kTN) * kBK;     // bytes per LDS stage
-static_assert(kTM == kFp8BM, "row tiles of the tile table");
-static_assert(kTN / 2 == kFp8BNH && kTN == kFp8BN2, "column tiles of the fp8 tile tables");
+// FP8 tile: 2 x 4 wavefronts of 8 x 4 blocks (128 x 64 each) -> 256 x 256
+constexpr int kWM8 = 2, kWN8 = 4, kMI8 = 8, kNI8 = 4;
+static_assert(kWM8 * kMI8 * 16 == kFp8BM, "row tiles of the fp8 tile table");
+static_assert(kWN8 * kNI8 * 16 == 2 * kFp8BNH && kWN8 * kNI8 * 16 == kFp8BN2, "column tiles");
 
 struct Fp8Params {
   const fp8_t* a_routed;    // gate/up: x_perm codes [P,H]; down: h codes [P,I]
@@ -78,10 +76,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(vm_wait_imm<N>());
 }
 
+// Waits until at most n slices' loads (PER each) of this wave are outstanding.
+template <int PER>
 __device__ __forceinline__ void wait_slices(int n) {
   if (n <= 0) wait_vm<0>();
-  else if (n == 1) wait_vm<kPer>();
-  else wait_vm<2 * kPer>();
+  else if (n == 1) wait_vm<PER>();
+  else wait_vm<2 * PER>();
 }
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -94,16 +94,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int 
 }
 #endif
 
-template <int MODE, int STAGES>
-__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
+__device__ __forceinline__ i32x8_t frag(const uint8_t* rowp, int r, int g) {
+  const i32x4v_t lo = *reinterpret_cast<const i32x4v_t*>(rowp + swz8(r, 2 * g) * 16);
+  const i32x4v_t hi = *reinterpret_cast<const i32x4v_t*>(rowp + swz8(r, 2 * g + 1) * 16);
+  return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+template <int MODE, int WM, int WN, int MI, int NI, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) {
+  constexpr int NW = WM * WN, NT = 64 * NW;
+  constexpr int BM = WM * MI * 16, BN = WN * NI * 16;
+  constexpr int BK = 128, CPR = BK / 16;
+  constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
+  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
+  constexpr int SA_W = BM / 64;                       // wavefronts that load activation scales
+  static_assert(BM % 64 == 0 && SA_W <= NW, "64 scale rows per loading wavefront");
+  constexpr int PER = A_CH + B_CH + 1;                // loads per thread per slice
+  static_assert(MODE != kGateUp8 || BN == 256, "a gate/up tile is one 1 x 128 tile of h");
+  static_assert(MODE != kDown8 || (128 % (NI * 16) == 0), "a wavefront's columns in one weight block");
+  // LDS layout (bytes): STAGES x [A rows | B rows | sa[BM] | dummy scale rows],
+  // then sw[2][kFp8MaxKC], then red[BM][WN]
+  constexpr int SA_OFF = (BM + BN) * BK;
+  constexpr int DUMMY_OFF = SA_OFF + BM * 4;
+  constexpr int STAGE = DUMMY_OFF + (NW - SA_W) * 256;
+  static_assert(STAGE % 16 == 0, "stage alignment");
+  constexpr int SW_OFF = STAGES * STAGE;
+  constexpr int RED_OFF = SW_OFF + 2 * kFp8MaxKC * 4;
+  constexpr int LDS_BYTES = RED_OFF + BM * WN * 4;
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * kStage];
-  __shared__ __attribute__((aligned(16))) float sa_lds[kTM * kFp8MaxKC];   // [row][chunk]
-  __shared__ float sw_lds[2 * kFp8MaxKC];                                  // [half][chunk]
-  __shared__ float red[kTM][kWN];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  float* sw_lds = reinterpret_cast<float*>(lds + SW_OFF);
+  float* red = reinterpret_cast<float*>(lds + RED_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / kWN, wn = wave % kWN;
+  const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, g = lane >> 4;
 
   // ------------------------------------------------------------ which tile
@@ -122,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
 
   // ------------------------------------------------------------ operands
   const int lda = MODE == kDown8 ? (shared ? p.S * p.I : p.I) : p.H;   // = K
-  const int K = lda, KC = K / 128;
+  const int KC = lda / 128;
   const fp8_t* A = (shared ? p.a_shared : p.a_routed) + (int64_t)row0 * lda;
   const float* SA = (shared ? p.sa_shared : p.sa_routed) + (int64_t)row0 * KC;
   const fp8_t* W;
@@ -139,14 +163,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
     ncols = p.H;
   }
 
-  // ------------------------------------------------------------ scales -> LDS
-  // activation scales of the tile's rows, all chunks: rows*KC contiguous floats
-  {
-    const int n = rows * KC;
-    for (int i = tid; i < kTM * KC; i += kThreads) sa_lds[i] = i < n ? SA[i] : 0.f;
-  }
-  // weight scales: [2][KC]; gate/up: gate block, up block; down: the tile's two
-  // 128-column output blocks
+  // ------------------------------------------------------------ weight scales -> LDS
+  // [2][KC]: gate/up: the gate block and the up block of this tile's 128 h
+  // columns; down: the tile's two 128-column output blocks
   if (tid < 2 * KC) {
     const int h = tid / KC, c = tid % KC;
     float v;
@@ -168,126 +187,133 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
   }
 
   // ------------------------------------------------------------ load offsets
-  int a_off[kACh], b_off[kBCh];
+  // Token rows past the valid ones get offsets outside the A (and scale)
+  // descriptors: the range check drops them without a memory request.
+  int a_off[A_CH], b_off[B_CH];
 #pragma unroll
-  for (int i = 0; i < kACh; ++i) {
-    const int q = (i * (kThreads / 64) + wave) * 64 + lane, r = q / kCPR, pc = q % kCPR;
-    // rows past the valid ones: offset outside the A descriptor (dropped, no request)
+  for (int i = 0; i < A_CH; ++i) {
+    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     a_off[i] = (r < rows ? r : rows + 1) * lda + swz8(r, pc) * 16;
   }
 #pragma unroll
-  for (int i = 0; i < kBCh; ++i) {
-    const int q = (i * (kThreads / 64) + wave) * 64 + lane, r = q / kCPR, pc = q % kCPR;
+  for (int i = 0; i < B_CH; ++i) {
+    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int wrow;
     if constexpr (MODE == kGateUp8) {
-      const bool up = r >= kTN / 2;
-      const int c = min(nt * (kTN / 2) + (up ? r - kTN / 2 : r), ncols - 1);
+      const bool up = r >= BN / 2;
+      const int c = min(nt * (BN / 2) + (up ? r - BN / 2 : r), ncols - 1);
       wrow = (c / p.I) * 2 * p.I + (up ? p.I : 0) + c % p.I;
     } else {
-      wrow = min(nt * kTN + r, ncols - 1);
+      wrow = min(nt * BN + r, ncols - 1);
     }
     b_off[i] = wrow * ldw + swz8(r, pc) * 16;
   }
+  const int sa_row = wave * 64 + lane;                 // scale row of this lane (SA_W waves)
+  const int sa_off = (wave < SA_W && sa_row < rows) ? sa_row * KC * 4 : (rows + 1) * KC * 4;
+  const int sa_dst = wave < SA_W ? SA_OFF + wave * 256 : DUMMY_OFF + (wave - SA_W) * 256;
   const __amdgpu_buffer_rsrc_t rsrc_a = rsrc_of(A, rows * lda);
   const __amdgpu_buffer_rsrc_t rsrc_w = rsrc_of(W, w_bytes);
+  const __amdgpu_buffer_rsrc_t rsrc_s = rsrc_of(SA, rows * KC * 4);
   const int64_t seg_kstride = (int64_t)p.H * p.I;   // down, shared: next expert's W_d every I of K
   typedef __attribute__((address_space(3))) void lds_void_t;
-#define MOE_ISSUE8(stage_, k0_)                                                                     \
-  {                                                                                                 \
-    const int k0v = (k0_);                                                                          \
-    const int wk = MODE == kDown8 ? (int)((k0v / p.I) * seg_kstride) + (k0v % p.I) : k0v;           \
-    uint8_t* sb = lds + (stage_) * kStage;                                                          \
-    _Pragma("unroll") for (int i = 0; i < kACh; ++i)                                                \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
-            rsrc_a, (lds_void_t*)(sb + (i * (kThreads / 64) + wave) * 1024), 16, a_off[i], k0v, 0, 0); \
-    _Pragma("unroll") for (int i = 0; i < kBCh; ++i)                                                \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                   \
-            rsrc_w, (lds_void_t*)(sb + kTM * kBK + (i * (kThreads / 64) + wave) * 1024), 16,        \
-            b_off[i], wk, 0, 0);                                                                    \
+#define MOE_ISSUE8(stage_, kc_)                                                                      \
+  {                                                                                                  \
+    const int kcv = (kc_), k0v = kcv * BK;                                                           \
+    const int wk = MODE == kDown8 ? (int)((k0v / p.I) * seg_kstride) + (k0v % p.I) : k0v;            \
+    uint8_t* sb = lds + (stage_) * STAGE;                                                            \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                 \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sb + (i * NW + wave) * 1024), \
+                                                 16, a_off[i], k0v, 0, 0);                          \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+            rsrc_w, (lds_void_t*)(sb + BM * BK + (i * NW + wave) * 1024), 16, b_off[i], wk, 0, 0);   \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_void_t*)(sb + sa_dst), 4, sa_off, kcv * 4, \
+                                             0, 0);                                                  \
   }
 
   const int nk = KC;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) MOE_ISSUE8(s, s * kBK);
-  // the scale stores above must be complete before any wavefront reads them
-  // (this also waits for the first stage, which slice 0 waits for anyway)
+    if (s < nk) MOE_ISSUE8(s, s);
+  // the weight-scale stores above are complete before any wavefront reads them
   __syncthreads();
 
-  f32x4_t acc[kMI][kNI];
+  f32x4_t acc[MI][NI];
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // LDS rows of this lane's operands; lane group g supplies K bytes [32g, 32g+32)
-  int a_rd[kMI], b_rd[kNI];
+  const int arow0 = wm * MI * 16 + l16;
+  int b_rd[NI];
 #pragma unroll
-  for (int mi = 0; mi < kMI; ++mi) a_rd[mi] = wm * kMI * 16 + mi * 16 + l16;
-#pragma unroll
-  for (int ni = 0; ni < kNI; ++ni) {
+  for (int ni = 0; ni < NI; ++ni) {
     int brow;
     if constexpr (MODE == kGateUp8) {
-      // blocks 0,1: gate rows of h columns wn*32 + [0,32); blocks 2,3: the matching up rows
-      brow = (ni < 2 ? 0 : kTN / 2) + wn * 32 + (ni & 1) * 16;
+      // blocks [0, NI/2): gate rows of h columns wn*NI/2*16 + ...; [NI/2, NI): the matching up rows
+      constexpr int HALF = NI / 2;
+      brow = (ni < HALF ? 0 : BN / 2) + wn * HALF * 16 + (ni % HALF) * 16;
     } else {
-      brow = wn * kNI * 16 + ni * 16;
+      brow = wn * NI * 16 + ni * 16;
     }
     b_rd[ni] = brow + l16;
   }
   // rows of this lane's accumulators: 4g + r inside each 16-row block
-  const int srow0 = wm * kMI * 16 + 4 * g;
-  const int wsel = MODE == kDown8 ? (wn >> 1) : 0;   // down: output block of this wavefront
+  const int srow0 = wm * MI * 16 + 4 * g;
+  const int wsel = MODE == kDown8 ? (wn * NI * 16) / 128 : 0;   // down: output block of this wavefront
+  const bool has_rows = wm * MI * 16 < rows;
 
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    wait_slices(min(nk - 1, kt + STAGES - 2) - kt);
+    wait_slices<PER>(min(nk - 1, kt + STAGES - 2) - kt);
     asm volatile("s_barrier" ::: "memory");
-    // All LDS reads of this slice come before the next slice's loads are
-    // issued: an LDS read placed after a direct-to-LDS load makes the compiler
-    // wait for that load (it cannot tell the stages apart).
-    const uint8_t* base = lds + cur * kStage;
-    i32x8_t fa[kMI], fb[kNI];
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      const uint8_t* rp = base + a_rd[mi] * kBK;
-      const int4 lo = *reinterpret_cast<const int4*>(rp + swz8(a_rd[mi], 2 * g) * 16);
-      const int4 hi = *reinterpret_cast<const int4*>(rp + swz8(a_rd[mi], 2 * g + 1) * 16);
-      fa[mi] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-#pragma unroll
-    for (int ni = 0; ni < kNI; ++ni) {
-      const uint8_t* rp = base + kTM * kBK + b_rd[ni] * kBK;
-      const int4 lo = *reinterpret_cast<const int4*>(rp + swz8(b_rd[ni], 2 * g) * 16);
-      const int4 hi = *reinterpret_cast<const int4*>(rp + swz8(b_rd[ni], 2 * g + 1) * 16);
-      fb[ni] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-    // combined scales of this chunk for the lane's 16 rows (x2 weight halves for gate/up)
-    float s0[kMI][4], s1[kMI][4];
-    const float w0 = sw_lds[wsel * kFp8MaxKC + kt];
-    const float w1 = sw_lds[kFp8MaxKC + kt];
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float a = sa_lds[(srow0 + mi * 16 + r) * KC + kt];
-        s0[mi][r] = a * w0;
-        s1[mi][r] = a * w1;
-      }
     if (kt + STAGES - 1 < nk) {
       const int st = cur == 0 ? STAGES - 1 : cur - 1;
-      MOE_ISSUE8(st, (kt + STAGES - 1) * kBK);
+      MOE_ISSUE8(st, kt + STAGES - 1);
     }
+    if (has_rows) {
+      const uint8_t* base = lds + cur * STAGE;
+      const float* sa_st = reinterpret_cast<const float*>(base + SA_OFF);
+      const float w0 = sw_lds[wsel * kFp8MaxKC + kt];
+      const float w1 = sw_lds[kFp8MaxKC + kt];
+      i32x8_t fb[NI];
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+      for (int ni = 0; ni < NI; ++ni) fb[ni] = frag(base + BM * BK + b_rd[ni] * BK, b_rd[ni], g);
+      // row blocks one at a time (short live ranges); the next block's operand
+      // and scale reads are issued before this block's MFMAs
+      i32x8_t fa = frag(base + arow0 * BK, arow0, g);
+      f32x4_t sa4 = *reinterpret_cast<const f32x4_t*>(sa_st + srow0);
 #pragma unroll
-      for (int ni = 0; ni < kNI; ++ni) {
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[mi], fb[ni], z, 0, 0, 0, 0, 0, 0);
-        const bool second = MODE == kGateUp8 && ni >= 2;
+      for (int mi = 0; mi < MI; ++mi) {
+        i32x8_t fa_n;
+        f32x4_t sa_n;
+        if (mi + 1 < MI) {
+          fa_n = frag(base + (arow0 + (mi + 1) * 16) * BK, arow0 + (mi + 1) * 16, g);
+          sa_n = *reinterpret_cast<const f32x4_t*>(sa_st + srow0 + (mi + 1) * 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float s0[4], s1[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(part[r], second ? s1[mi][r] : s0[mi][r], acc[mi][ni][r]);
+        for (int r = 0; r < 4; ++r) {
+          s0[r] = sa4[r] * w0;
+          s1[r] = sa4[r] * w1;
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[ni], z, 0, 0, 0, 0, 0, 0);
+          const bool second = MODE == kGateUp8 && ni >= NI / 2;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(part[r], second ? s1[r] : s0[r], acc[mi][ni][r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (mi + 1 < MI) {
+          fa = fa_n;
+          sa4 = sa_n;
+        }
       }
+    }
     cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
 #undef MOE_ISSUE8
@@ -295,61 +321,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_kernel(Fp8Params p) {
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] holds C[i][j] with j = lane % 16, i = 4 * (lane / 16) + r
   if constexpr (MODE == kGateUp8) {
-    float h[kMI][4][2];
-    float pmax[kMI][4];
+    constexpr int HALF = NI / 2;
+    // per row: SwiGLU in registers, amax over this wavefront's HALF*16 columns
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float m = 0.f;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const float gv = acc[mi][b][r], uv = acc[mi][b + 2][r];
-          h[mi][r][b] = gv / (1.0f + expf(-gv)) * uv;
-          m = fmaxf(m, fabsf(h[mi][r][b]));
+        for (int b = 0; b < HALF; ++b) {
+          const float gv = acc[mi][b][r], uv = acc[mi][b + HALF][r];
+          const float h = gv / (1.0f + expf(-gv)) * uv;
+          acc[mi][b][r] = h;     // h replaces the gate accumulator
+          m = fmaxf(m, fabsf(h));
         }
 #pragma unroll
         for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        pmax[mi][r] = m;
+        if (l16 == 0) red[(srow0 + mi * 16 + r) * WN + wn] = m;
       }
-    if (l16 == 0) {
-#pragma unroll
-      for (int mi = 0; mi < kMI; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[srow0 + mi * 16 + r][wn] = pmax[mi][r];
-    }
     __syncthreads();
     fp8_t* out = static_cast<fp8_t*>(shared ? p.out_shared : p.out_routed);
     float* out_s = shared ? p.out_shared_scale : p.out_routed_scale;
     const int ntile = ncols / 128;
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = srow0 + mi * 16 + r;
         if (i >= rows) continue;
-        const float amax = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
+        float amax = red[i * WN];
+#pragma unroll
+        for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[i * WN + w2]);
         const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
         const int64_t row = row0 + i;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int col = nt * 128 + wn * 32 + b * 16 + l16;
-          if (col < ncols) out[row * ncols + col] = f32_to_e4m3(__fdiv_rn(h[mi][r][b], sc));
+        for (int b = 0; b < HALF; ++b) {
+          const int col = nt * 128 + wn * HALF * 16 + b * 16 + l16;
+          if (col < ncols) out[row * ncols + col] = f32_to_e4m3(__fdiv_rn(acc[mi][b][r], sc));
         }
         if (wn == 0 && l16 == 0) out_s[row * ntile + nt] = sc;
       }
   } else {
     bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
 #pragma unroll
-    for (int mi = 0; mi < kMI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = srow0 + mi * 16 + r;
         if (i >= rows) continue;
         const int64_t row = row0 + i;
 #pragma unroll
-        for (int ni = 0; ni < kNI; ++ni) {
-          const int col = nt * kTN + wn * kNI * 16 + ni * 16 + l16;
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = nt * BN + wn * NI * 16 + ni * 16 + l16;
           if (col < ncols) out[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
         }
       }
@@ -371,6 +394,7 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
   float* hss = reinterpret_cast<float*>(base + L.off_hss);
   fp8_t* xq = reinterpret_cast<fp8_t*>(base + L.off_xq);
   float* xqs = reinterpret_cast<float*>(base + L.off_xqs);
+  constexpr int kThreads8 = 64 * kWM8 * kWN8;
   moe_status s;
   Fp8Params p{};
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
@@ -387,7 +411,8 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.ntiles = hdr;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, 2>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
+                         dim3(kThreads8), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -402,7 +427,8 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.ntiles = hdr + 1;
     const int64_t grid = align_up((size_t)L.max2, 8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, 2>), dim3((unsigned)grid), dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
+                         dim3(kThreads8), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
