@@ -5,6 +5,8 @@
 //
 // This file holds the entry point, the device-side tile-table builder of the
 // grouped GEMMs, and the fp32 expert kernels of the small fp32 configuration.
+#include <algorithm>
+
 #include "common.h"
 #include "ffn_layout.h"
 #include "kernels.h"
@@ -21,7 +23,8 @@ namespace moe {
 // on one XCD (consecutive entries) then cover a few row tiles times a few
 // column tiles, so both their activation rows and their weight rows are
 // shared in that XCD's L2, also for segments far larger than the number of
-// tiles in flight.  One workgroup; exclusive prefix sums over segments in LDS.
+// tiles in flight.  Every workgroup computes the prefix sums over segments in LDS
+// (at most 513 segments) and writes its own share of the entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int S, int T, int bm1, int bm2, int nt1, int nt1s,
                                                            int nt2,
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   pre1[tid] = inc1 - c1;
   pre2[tid] = inc2 - c2;
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0 && blockIdx.x == 0) {
     hdr[0] = total1;
     hdr[1] = total2;
   }
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     const int* pre = pass == 0 ? pre1 : pre2;
     const int total = pass == 0 ? total1 : total2;
     TileDesc* out = pass == 0 ? t1 : t2;
-    for (int L = tid; L < total; L += 1024) {
+    for (int L = blockIdx.x * 1024 + tid; L < total; L += gridDim.x * 1024) {
       int lo = 0, hi = nseg;           // last g with pre[g] <= L and a non-empty segment
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -100,7 +103,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm1, L.bm2,
+  const int64_t most = L.max1 > L.max2 ? L.max1 : L.max2;
+  const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((most + 1023) / 1024, 1), 64);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(blocks), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm1, L.bm2,
                      (int)L.nt1, (int)L.nt1s, (int)L.nt2,
                      reinterpret_cast<TileDesc*>(base + L.off_t1),
                      reinterpret_cast<TileDesc*>(base + L.off_t2),
