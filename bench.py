@@ -264,6 +264,39 @@ def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
     return out
 
 
+def small_workload(name, steps, warmup, balance_steps):
+    """One of the small configurations (tiny fp32, mid bf16): per-step time, rates, and
+    the max/mean load over `balance_steps` batches (fresh x from the shared generator)."""
+    import torch
+
+    from biased_top_routing_amd.runner import MoeLayerGPU
+    from workloads import CONFIGS
+    from workloads.inputs import make_weights, make_x
+    c = CONFIGS[name]
+    w = make_weights(c)
+    layer = MoeLayerGPU(c, w)
+    x = to_dev(make_x(c, 0))
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    ms, stage_ms = time_layer(layer, x, bias, c, steps, warmup)
+    flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
+    peak = 157.3 if c.act == "f32" else PEAK_BF16_TFLOPS   # fp32 vector (no MFMA used) / bf16 MFMA
+    out = {"workload": c.name, "T": c.T, "ms_per_step": round(ms, 4), "tokens_per_s": round(c.T / (ms * 1e-3), 1),
+           "pairs_per_s": round(c.T * c.k / (ms * 1e-3), 1),
+           "layer_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+           "layer_frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
+           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    ratios = []
+    mean = c.T * c.k / c.E
+    for step in range(balance_steps):
+        layer.forward(to_dev(make_x(c, step)), bias, gamma=c.gamma)
+        ratios.append(float(layer.counts.max().item()) / mean)
+    out["balance"] = {"steps": balance_steps,
+                      "max_over_mean_at_step": {str(i): round(ratios[i - 1], 3)
+                                                for i in (1, 5, 10, 25, 50) if i <= balance_steps}}
+    return out
+
+
 def gemm_summary(c, ms_per_step, stage_ms):
     peak = PEAK_FP8_TFLOPS if c.wgt == "fp8_e4m3" else PEAK_BF16_TFLOPS
     gu = c.gate_up_flops() / (stage_ms["gate_up"] * 1e-3) / 1e12
@@ -350,8 +383,11 @@ def main():
             "flops_per_launch": c.gate_up_flops(),
             "avg_launch_ms": round(stage_ms["gate_up"], 4),
         },
+        "pairs_per_s": round(c.T * c.k / (ms_per_step * 1e-3), 1),
         "stages": {
             "ms": {k: round(v, 4) for k, v in stage_ms.items()},
+            "gate_up_tflops": round(gu_tflops, 2),
+            "layer_frac_of_peak": round(total_flops / (ms_per_step * 1e-3) / 1e12 / peak, 4),
             "down_tflops": round(dn_tflops, 2),
             "layer_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 2),
             "route_gbs": round(route_gbs, 1),
@@ -380,6 +416,7 @@ def main():
         cnt = lf.counts.cpu().numpy()
         extras["v3_fp8"] = {"workload": cf.name, "T": cf.T, "ms_per_step": round(msf, 4),
                             "tokens_per_s": round(cf.T / (msf * 1e-3), 1),
+                            "pairs_per_s": round(cf.T * cf.k / (msf * 1e-3), 1),
                             "gate_up_tflops": round(gu8, 2), "gate_up_frac_fp8_peak": round(gu8 / pk, 4),
                             "down_tflops": round(dn8, 2), "down_frac_fp8_peak": round(dn8 / pk, 4),
                             "layer_tflops": round((cf.gate_up_flops() + cf.down_flops() + cf.router_flops()) /
@@ -390,6 +427,10 @@ def main():
         extras["v3_fp8"]["balance"] = balance_trajectory(lf, cf, wf, cf.steps)
         del lf, xf
         torch.cuda.empty_cache()
+        for name in ("tiny_fp32", "mid_bf16"):
+            log(f"extra: {name}")
+            cs = CONFIGS[name]
+            extras[name] = small_workload(name, 50, 5, cs.steps)
         out["other_workloads"] = extras
     if not args.no_cpu_baseline and not fp8:
         log("timing the CPU oracle on a bounded sample")
