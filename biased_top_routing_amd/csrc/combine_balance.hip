@@ -10,7 +10,8 @@
 
 namespace moe {
 
-// One wavefront per token; 16-byte chunks (8 bf16 or 4 fp32 values) per lane.
+// One workgroup per token (its row's 16-byte chunks spread over 256 lanes;
+// 8 bf16 or 4 fp32 values per chunk).
 // y = y_shared + sum_j w_j * y_perm[inv_j], fp32 accumulation, j ascending.
 // The k routed rows of a chunk are loaded in batches of 8 before they are
 // accumulated, so that a lane keeps up to 9 loads in flight.  Each output row
@@ -60,12 +61,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       uint4* __restrict__ y) {
   constexpr int KB = 8;   // routed rows loaded per batch
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t t = blockIdx.x;          // the whole workgroup on one token
+  const int c0 = threadIdx.x, cstep = blockDim.x;
   if (t >= T) return;
   const int32_t myp = lane < k ? inv[t * k + lane] : 0;
   const float myw = lane < k ? topk_w[t * k + lane] : 0.f;
   constexpr int V = BF16 ? 8 : 4;
-  for (int64_t c = lane; c < nchunk; c += kWave) {
+  for (int64_t c = c0; c < nchunk; c += cstep) {
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
@@ -122,7 +124,7 @@ extern "C" moe_status moe_combine(const moe_cfg* cfg, const void* y_perm, const 
   if (cfg->S > 0 && !y_shared) return MOE_ERR_NULL;
   if (cfg->T == 0) return MOE_OK;
   const int64_t nchunk = (int64_t)cfg->H * act_bytes(cfg) / 16;
-  const dim3 grid((unsigned)((cfg->T + 3) / 4));
+  const dim3 grid((unsigned)cfg->T);
   const uint4* ysh = cfg->S > 0 ? (const uint4*)y_shared : nullptr;
   if (cfg->act == MOE_F32)
     hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, as_stream(stream), (const uint4*)y_perm,
