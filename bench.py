@@ -45,18 +45,24 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode-size and FP8 measurements that follow the headline one")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
+    ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
+                    help="gather: dispatch writes the indices and the gate/up GEMM reads its rows from x "
+                         "through perm; copy: dispatch also writes x_perm and the GEMM reads that")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size 3 times (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
-def stage_bytes(c):
-    """Algorithmic HBM bytes of the bandwidth-bound stages (per layer pass)."""
+def stage_bytes(c, gather=False):
+    """Algorithmic HBM bytes of the bandwidth-bound stages (per layer pass).  With
+    gather, dispatch moves indices only (the rows are read by the gate/up GEMM)."""
     a = 2  # bf16
     route = c.T * c.E * 4 + c.E * 4 + c.T * c.k * 8                      # scores in, bias, idx + w out
     router = c.T * c.H * a + c.E * c.H * a + c.T * c.E * 4                # x + W_r in, scores out
-    dispatch = c.T * c.H * a + c.T * c.k * c.H * a + c.T * c.k * 4 * 4   # x in, x_perm out, idx in, perm/inv out
+    dispatch = c.T * c.k * 4 * 4                                          # idx in (twice), perm + inv out
+    if not gather:
+        dispatch += c.T * c.H * a + c.T * c.k * c.H * a                   # x in, x_perm out
     combine = c.T * c.k * c.H * a + c.T * c.H * a * (2 if c.S else 1) + c.T * c.k * 8
     return dict(router=router, topk=route, dispatch=dispatch, combine=combine)
 
@@ -264,7 +270,7 @@ def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
     return out
 
 
-def small_workload(name, steps, warmup, balance_steps):
+def small_workload(name, steps, warmup, balance_steps, gather=False):
     """One of the small configurations (tiny fp32, mid bf16): per-step time, rates, and
     the max/mean load over `balance_steps` batches (fresh x from the shared generator)."""
     import torch
@@ -274,7 +280,7 @@ def small_workload(name, steps, warmup, balance_steps):
     from workloads.inputs import make_weights, make_x
     c = CONFIGS[name]
     w = make_weights(c)
-    layer = MoeLayerGPU(c, w)
+    layer = MoeLayerGPU(c, w, gather=gather)
     x = to_dev(make_x(c, 0))
     bias = torch.from_numpy(w.bias0.copy()).cuda()
     ms, stage_ms = time_layer(layer, x, bias, c, steps, warmup)
@@ -332,11 +338,12 @@ def main():
     w = make_weights(c)
     xh = make_x(c, 0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
-    layer = MoeLayerGPU(c, w)
+    gather = args.dispatch == "gather"
+    layer = MoeLayerGPU(c, w, gather=gather)
     x = to_dev(xh)
     bias = torch.from_numpy(w.bias0.copy()).cuda()
     torch.cuda.synchronize()
-    log(f"uploaded; timing {args.steps} steps after {args.warmup} warm-up steps")
+    log(f"uploaded; timing {args.steps} steps after {args.warmup} warm-up steps (dispatch: {args.dispatch})")
     ms_per_step, stage_ms = time_layer(layer, x, bias, c, args.steps, args.warmup)
     value = c.T / (ms_per_step * 1e-3)
     counts = layer.counts.cpu().numpy()
@@ -353,7 +360,7 @@ def main():
 
     peak, gu_tflops, dn_tflops = gemm_summary(c, ms_per_step, stage_ms)
     total_flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
-    b = stage_bytes(c)
+    b = stage_bytes(c, gather)
     route_gbs = (b["router"] + b["topk"]) / (stage_ms["route"] * 1e-3) / 1e9
     fp8 = c.wgt == "fp8_e4m3"
     out = {
@@ -370,7 +377,8 @@ def main():
         "dtype": "fp8_e4m3 experts, bf16 router" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": c.name, "T": c.T, "H": c.H, "E": c.E, "G": c.G, "M": c.M, "k": c.k, "S": c.S,
-                   "I": c.I, "route_scale": c.route_scale, "parallelism": "single-gpu"},
+                   "I": c.I, "route_scale": c.route_scale, "parallelism": "single-gpu",
+                   "dispatch": args.dispatch},
         "roofline": {
             "kernel": ("gemm_fp8_kernel<gate_up>" if fp8 else "gemm_bf16_kernel<gate_up>") +
                       " (routed + shared gate/up GEMM with fused SwiGLU)",
@@ -408,7 +416,7 @@ def main():
         cf = CONFIGS["v3_fp8"]
         log("extra: the FP8 layer (T=32768, Zipf-skewed routing)")
         wf = make_weights(cf)
-        lf = MoeLayerGPU(cf, wf)
+        lf = MoeLayerGPU(cf, wf, gather=gather)
         xf = to_dev(make_x(cf, 0))
         bf = torch.from_numpy(wf.bias0.copy()).cuda()
         msf, stf = time_layer(lf, xf, bf, cf, args.steps, args.warmup)
@@ -430,7 +438,7 @@ def main():
         for name in ("tiny_fp32", "mid_bf16"):
             log(f"extra: {name}")
             cs = CONFIGS[name]
-            extras[name] = small_workload(name, 50, 5, cs.steps)
+            extras[name] = small_workload(name, 50, 5, cs.steps, gather)
         out["other_workloads"] = extras
     if not args.no_cpu_baseline and not fp8:
         log("timing the CPU oracle on a bounded sample")

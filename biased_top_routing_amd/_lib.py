@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
             "moe_dispatch": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_expert_ffn": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp, sz,
                                ctypes.c_int, vp],
+            "moe_expert_ffn_gather": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, sz,
+                                      ctypes.c_int, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_update_bias": [cfgp, vp, vp, f32, vp],
             "moe_quantize_fp8": [vp, i32, i32, i32, i32, vp, vp, vp],
@@ -150,6 +152,13 @@ def moe_expert_ffn(cfg, x_perm, x_perm_scale, offsets, weights: MoeExpertWeights
     _check("moe_expert_ffn", lib().moe_expert_ffn(ctypes.byref(cfg), _p(x_perm), _p(x_perm_scale), _p(offsets),
                                                   ctypes.byref(weights), _p(x), _p(y_perm), _p(y_shared),
                                                   _p(ws), _nbytes(ws), phase, _s(stream)))
+
+
+def moe_expert_ffn_gather(cfg, x, perm, offsets, weights: MoeExpertWeights, y_perm, y_shared, ws,
+                          phase=MOE_FFN_ALL, stream=None):
+    _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
+        ctypes.byref(cfg), _p(x), _p(perm), _p(offsets), ctypes.byref(weights), _p(y_perm), _p(y_shared),
+        _p(ws), _nbytes(ws), phase, _s(stream)))
 
 
 def moe_combine(cfg, y_perm, y_shared, inv, topk_w, y, stream=None):

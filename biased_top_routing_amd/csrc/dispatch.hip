@@ -329,8 +329,9 @@ extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, 
   moe_status st = validate_cfg(cfg);
   if (st != MOE_OK) return st;
   const bool fp8 = cfg->wgt == MOE_FP8_E4M3;
-  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !x_perm || !ws) return MOE_ERR_NULL;
-  if (fp8 && !x_perm_scale) return MOE_ERR_NULL;
+  // x_perm == nullptr: indices only (the expert FFN gathers the rows itself)
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !ws) return MOE_ERR_NULL;
+  if (x_perm && (!x || (fp8 && !x_perm_scale))) return MOE_ERR_NULL;
   if (ws_bytes < dispatch_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
   const int64_t N = pairs(cfg);
@@ -355,6 +356,7 @@ extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, 
   hipLaunchKernelGGL(rank_kernel, dim3(blocks), dim3(256), 4 * E * sizeof(int32_t), s, topk_idx, N, E,
                      nbits, nseg, segc, offsets, perm, inv);
   if ((st = launch_status()) != MOE_OK) return st;
+  if (!x_perm) return MOE_OK;
   const unsigned tblocks = (unsigned)((cfg->T + 3) / 4);
   if (fp8) {
     hipLaunchKernelGGL((permute_rows_fp8_kernel<8>), dim3(tblocks), dim3(256), 0, s, (const uint4*)x, inv,

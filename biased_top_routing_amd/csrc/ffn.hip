@@ -127,7 +127,10 @@ __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int6
 
 // h[row, c] = silu(<a_row, Wg_c>) * <a_row, Wu_c>; one thread per (row, c).
 // offsets == nullptr: shared experts (h width S*I, column c -> expert c / I).
+// rowmap != nullptr: operand row `row` is row rowmap[row] / k of a (the
+// expert-sorted order gathered from x).
 __global__ __launch_bounds__(256) void gateup_f32_kernel(const float* __restrict__ a, int64_t nrows,
+                                                         const int32_t* __restrict__ rowmap, int k,
                                                          const int32_t* __restrict__ offsets, int E,
                                                          const float* __restrict__ W, int H, int I,
                                                          int hw, float* __restrict__ h) {
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(const float* __restrict
   const int cc = c % I;
   const float* wg = W + ((int64_t)ex * 2 * I + cc) * H;
   const float* wu = wg + (int64_t)I * H;
-  const float4* ar = reinterpret_cast<const float4*>(a + row * H);
+  const int64_t arow = rowmap ? (int64_t)(rowmap[row] / k) : row;
+  const float4* ar = reinterpret_cast<const float4*>(a + arow * H);
   float g = 0.f, u = 0.f;
   for (int i = 0; i < H / 4; ++i) {
     const float4 x = ar[i];
@@ -175,9 +179,9 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
   y[row * H + n] = acc;
 }
 
-moe_status launch_ffn_f32(const moe_cfg* c, const float* x_perm, const int32_t* offsets,
-                          const moe_expert_weights* w, const float* x, float* y_perm,
-                          float* y_shared, void* ws, int phase, hipStream_t st) {
+moe_status launch_ffn_f32(const moe_cfg* c, const float* x_perm, const int32_t* perm,
+                          const int32_t* offsets, const moe_expert_weights* w, const float* x,
+                          float* y_perm, float* y_shared, void* ws, int phase, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
   float* hp = reinterpret_cast<float*>(base + L.off_hp);
@@ -185,12 +189,12 @@ moe_status launch_ffn_f32(const moe_cfg* c, const float* x_perm, const int32_t* 
   const int64_t P = pairs(c);
   auto blocks = [](int64_t n) { return dim3((unsigned)((n + 255) / 256)); };
   if (phase == MOE_FFN_ALL || phase == MOE_FFN_GATE_UP) {
-    hipLaunchKernelGGL(gateup_f32_kernel, blocks(P * c->I), dim3(256), 0, st, x_perm, P, offsets, c->E,
-                       (const float*)w->w_gate_up, c->H, c->I, c->I, hp);
+    hipLaunchKernelGGL(gateup_f32_kernel, blocks(P * c->I), dim3(256), 0, st, perm ? x : x_perm, P, perm,
+                       c->k, offsets, c->E, (const float*)w->w_gate_up, c->H, c->I, c->I, hp);
     if (c->S > 0)
       hipLaunchKernelGGL(gateup_f32_kernel, blocks((int64_t)c->T * c->S * c->I), dim3(256), 0, st, x,
-                         (int64_t)c->T, (const int32_t*)nullptr, c->E, (const float*)w->ws_gate_up, c->H,
-                         c->I, c->S * c->I, hs);
+                         (int64_t)c->T, (const int32_t*)nullptr, 1, (const int32_t*)nullptr, c->E,
+                         (const float*)w->ws_gate_up, c->H, c->I, c->S * c->I, hs);
   }
   if (phase == MOE_FFN_ALL || phase == MOE_FFN_DOWN) {
     hipLaunchKernelGGL(down_f32_kernel, blocks(P * c->H), dim3(256), 0, st, hp, P, offsets, c->E,
@@ -207,28 +211,60 @@ moe_status launch_ffn_f32(const moe_cfg* c, const float* x_perm, const int32_t* 
 
 using namespace moe;
 
-extern "C" moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
-                                     const int32_t* offsets, const moe_expert_weights* w, const void* x,
-                                     void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
-                                     void* stream) {
+namespace {
+
+// Both FFN entry points: routed gate/up rows from x_perm (perm == nullptr) or
+// gathered from x through perm.
+moe_status expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                      const int32_t* perm, const int32_t* offsets, const moe_expert_weights* w,
+                      const void* x, void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
+                      void* stream) {
   moe_status st = validate_cfg(cfg);
   if (st != MOE_OK) return st;
   if (phase != MOE_FFN_ALL && phase != MOE_FFN_GATE_UP && phase != MOE_FFN_DOWN)
     return MOE_ERR_UNSUPPORTED;
-  if (!w || !x_perm || !offsets || !y_perm || !ws || !w->w_gate_up || !w->w_down) return MOE_ERR_NULL;
+  const bool gate_up = phase != MOE_FFN_DOWN;
+  if (!w || !offsets || !y_perm || !ws || !w->w_gate_up || !w->w_down) return MOE_ERR_NULL;
+  if (!perm && !x_perm) return MOE_ERR_NULL;
+  if (perm && gate_up && !x) return MOE_ERR_NULL;
   if (cfg->S > 0 && (!x || !y_shared || !w->ws_gate_up || !w->ws_down)) return MOE_ERR_NULL;
   const bool fp8 = cfg->wgt == MOE_FP8_E4M3;
-  if (fp8 && (!x_perm_scale || !w->w_gate_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
+  if (fp8 && ((!perm && !x_perm_scale) || !w->w_gate_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
   if (fp8 && cfg->S > 0 && (!w->ws_gate_up_scale || !w->ws_down_scale)) return MOE_ERR_NULL;
+  // gathered rows are addressed by 32-bit byte offsets into x (one row past
+  // the end marks a dropped row)
+  if (perm && cfg->act != MOE_F32 &&
+      ((int64_t)cfg->T + 1) * cfg->H * (fp8 ? 1 : (int64_t)act_bytes(cfg)) > INT32_MAX)
+    return MOE_ERR_UNSUPPORTED;
   if (ws_bytes < FfnLayout(cfg).total) return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
   if (cfg->act == MOE_F32)
-    return launch_ffn_f32(cfg, (const float*)x_perm, offsets, w, (const float*)x, (float*)y_perm,
+    return launch_ffn_f32(cfg, (const float*)x_perm, perm, offsets, w, (const float*)x, (float*)y_perm,
                           (float*)y_shared, ws, phase, s);
   if (!fp8)
-    return launch_ffn_bf16(cfg, (const bf16_t*)x_perm, offsets, w, (const bf16_t*)x, (bf16_t*)y_perm,
-                           (bf16_t*)y_shared, ws, phase, s);
-  return launch_ffn_fp8(cfg, (const fp8_t*)x_perm, x_perm_scale, offsets, w, (const bf16_t*)x,
+    return launch_ffn_bf16(cfg, (const bf16_t*)x_perm, perm, offsets, w, (const bf16_t*)x,
+                           (bf16_t*)y_perm, (bf16_t*)y_shared, ws, phase, s);
+  return launch_ffn_fp8(cfg, (const fp8_t*)x_perm, x_perm_scale, perm, offsets, w, (const bf16_t*)x,
                         (bf16_t*)y_perm, (bf16_t*)y_shared, ws, phase, s);
+}
+
+}  // namespace
+
+extern "C" moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
+                                     const int32_t* offsets, const moe_expert_weights* w, const void* x,
+                                     void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
+                                     void* stream) {
+  if (!x_perm) return MOE_ERR_NULL;
+  return expert_ffn(cfg, x_perm, x_perm_scale, nullptr, offsets, w, x, y_perm, y_shared, ws, ws_bytes,
+                    phase, stream);
+}
+
+extern "C" moe_status moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* perm,
+                                            const int32_t* offsets, const moe_expert_weights* w,
+                                            void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                                            int phase, void* stream) {
+  if (!perm) return MOE_ERR_NULL;
+  return expert_ffn(cfg, nullptr, nullptr, perm, offsets, w, x, y_perm, y_shared, ws, ws_bytes, phase,
+                    stream);
 }

@@ -41,7 +41,8 @@ struct GemmParams {
   void* out_shared;         // gate/up: h_shared; down: y_shared
   const TileDesc* tiles;
   const int32_t* ntiles;
-  int T, H, E, S, I;
+  const int32_t* perm;      // gate/up: non-null -> routed rows gathered from a_shared
+  int T, H, E, S, I, k;
 };
 
 // s_waitcnt immediate that waits until at most N vector-memory operations of
@@ -132,6 +133,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     nt = __builtin_amdgcn_readfirstlane(d.nt);
   }
   const bool shared = (MODE != kRouter) && seg == p.E;
+  // Routed gate/up rows gathered straight from x: row row0 + r of the
+  // expert-sorted order is token perm[row0 + r] / k (dispatch's row copy
+  // folded into the operand loads).
+  const bool gather = MODE == kGateUp && !shared && p.perm != nullptr;
 
   // ------------------------------------------------------------ operand bases
   const bf16_t* A;
@@ -140,11 +145,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     A = shared ? p.a_shared : p.a_routed;
     lda = shared ? p.S * p.I : p.I;
   } else {
-    A = (MODE == kRouter || shared) ? p.a_shared : p.a_routed;
+    A = (MODE == kRouter || shared || gather) ? p.a_shared : p.a_routed;
     lda = p.H;
   }
   const int K = lda;
-  A += (int64_t)row0 * lda;
+  if (!gather) A += (int64_t)row0 * lda;
+  const int a_rows = gather ? p.T : rows;   // rows covered by the A descriptor
 
   const bf16_t* W;
   int ldw;
@@ -176,7 +182,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
-    a_off[i] = (r < rows ? r : rows + 1) * lda + swz<CPR>(r, pc) * 8;
+    int src = r < rows ? r : a_rows + 1;
+    if constexpr (MODE == kGateUp)
+      if (gather && r < rows) src = p.perm[row0 + r] / p.k;
+    a_off[i] = src * lda + swz<CPR>(r, pc) * 8;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
@@ -200,7 +209,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   if constexpr (MODE == kRouter) w_bytes = p.E * p.H * 2;
   else if constexpr (MODE == kGateUp) w_bytes = (shared ? p.S : 1) * 2 * p.I * p.H * 2;
   else w_bytes = (shared ? p.S : 1) * p.H * p.I * 2;
-  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, rows * lda * 2);
+  const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, a_rows * lda * 2);
   const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(W, w_bytes);
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) a_off[i] *= 2;
@@ -252,9 +261,15 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
 
   // Ring: slices kt+1 .. kt+STAGES-2 are in flight while slice kt is multiplied.
   const int nk = K / BK;
+  // Down GEMM: each tile starts its K walk at its own slice (3 per column
+  // tile, 1 per row tile) and wraps around, so that tiles sharing a weight or
+  // h panel do not all wait on the same cache misses at once (measured 2-3%
+  // faster).  Only the fp32 summation order of the slices depends on it.
+  const int rot = MODE == kDown ? (int)(((unsigned)nt * 3u + (unsigned)(row0 / BM)) % (unsigned)nk) : 0;
+  auto kslice = [&](int kt_) { const int q = kt_ + rot; return q >= nk ? q - nk : q; };
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) MOE_ISSUE(s, s * BK);
+    if (s < nk) MOE_ISSUE(s, kslice(s) * BK);
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of slice kt have landed once only the later slices remain
@@ -265,7 +280,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     asm volatile("s_barrier" ::: "memory");
     if (kt + STAGES - 1 < nk) {
       const int st = cur == 0 ? STAGES - 1 : cur - 1;   // (kt + STAGES - 1) % STAGES
-      MOE_ISSUE(st, (kt + STAGES - 1) * BK);
+      MOE_ISSUE(st, kslice(kt + STAGES - 1) * BK);
     }
     const bf16_t* base = lds + cur * STAGE;
     // Operand fragments are double-buffered across the BK/16 MFMA k-steps: the
@@ -363,9 +378,9 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   return launch_status();
 }
 
-moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t* offsets,
-                           const moe_expert_weights* w, const bf16_t* x, bf16_t* y_perm,
-                           bf16_t* y_shared, void* ws, int phase, hipStream_t st) {
+moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t* perm,
+                           const int32_t* offsets, const moe_expert_weights* w, const bf16_t* x,
+                           bf16_t* y_perm, bf16_t* y_shared, void* ws, int phase, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
   const int32_t* hdr = reinterpret_cast<const int32_t*>(base + L.off_hdr);
@@ -380,7 +395,8 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.out_routed = hp; p.out_shared = hs;
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t1);
     p.ntiles = hdr;
-    p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
+    p.perm = perm;
+    p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
     const int64_t grid = align_up((size_t)L.max1, 8);
     if (grid > 0) {
       if (L.dec)

@@ -61,7 +61,8 @@ struct Fp8Params {
   float* out_shared_scale;
   const TileDesc* tiles;
   const int32_t* ntiles;
-  int T, H, E, S, I;
+  const int32_t* perm;      // gate/up: non-null -> routed rows gathered from a_shared / sa_shared
+  int T, H, E, S, I, k;
 };
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
@@ -143,12 +144,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   const int rows = __builtin_amdgcn_readfirstlane(d.rows);
   const int nt = __builtin_amdgcn_readfirstlane(d.nt);
   const bool shared = seg == p.E;
+  // Routed gate/up rows gathered from the quantised x: row row0 + r of the
+  // expert-sorted order is token perm[row0 + r] / k (codes and scales).
+  const bool gather = MODE == kGateUp8 && !shared && p.perm != nullptr;
 
   // ------------------------------------------------------------ operands
   const int lda = MODE == kDown8 ? (shared ? p.S * p.I : p.I) : p.H;   // = K
   const int KC = lda / 128;
-  const fp8_t* A = (shared ? p.a_shared : p.a_routed) + (int64_t)row0 * lda;
-  const float* SA = (shared ? p.sa_shared : p.sa_routed) + (int64_t)row0 * KC;
+  const int64_t a_base = gather ? 0 : (int64_t)row0;
+  const fp8_t* A = (shared || gather ? p.a_shared : p.a_routed) + a_base * lda;
+  const float* SA = (shared || gather ? p.sa_shared : p.sa_routed) + a_base * KC;
+  const int a_rows = gather ? p.T : rows;   // rows covered by the A and scale descriptors
   const fp8_t* W;
   int ldw, w_bytes, ncols;
   if constexpr (MODE == kGateUp8) {
@@ -193,7 +199,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #pragma unroll
   for (int i = 0; i < A_CH; ++i) {
     const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
-    a_off[i] = (r < rows ? r : rows + 1) * lda + swz8(r, pc) * 16;
+    int src = r < rows ? r : a_rows + 1;
+    if constexpr (MODE == kGateUp8)
+      if (gather && r < rows) src = p.perm[row0 + r] / p.k;
+    a_off[i] = src * lda + swz8(r, pc) * 16;
   }
 #pragma unroll
   for (int i = 0; i < B_CH; ++i) {
@@ -209,11 +218,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     b_off[i] = wrow * ldw + swz8(r, pc) * 16;
   }
   const int sa_row = wave * 64 + lane;                 // scale row of this lane (SA_W waves)
-  const int sa_off = (wave < SA_W && sa_row < rows) ? sa_row * KC * 4 : (rows + 1) * KC * 4;
+  int sa_src = (wave < SA_W && sa_row < rows) ? sa_row : a_rows + 1;
+  if constexpr (MODE == kGateUp8)
+    if (gather && wave < SA_W && sa_row < rows) sa_src = p.perm[row0 + sa_row] / p.k;
+  const int sa_off = sa_src * KC * 4;
   const int sa_dst = wave < SA_W ? SA_OFF + wave * 256 : DUMMY_OFF + (wave - SA_W) * 256;
-  const __amdgpu_buffer_rsrc_t rsrc_a = rsrc_of(A, rows * lda);
+  const __amdgpu_buffer_rsrc_t rsrc_a = rsrc_of(A, a_rows * lda);
   const __amdgpu_buffer_rsrc_t rsrc_w = rsrc_of(W, w_bytes);
-  const __amdgpu_buffer_rsrc_t rsrc_s = rsrc_of(SA, rows * KC * 4);
+  const __amdgpu_buffer_rsrc_t rsrc_s = rsrc_of(SA, a_rows * KC * 4);
   const int64_t seg_kstride = (int64_t)p.H * p.I;   // down, shared: next expert's W_d every I of K
   typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_ISSUE8(stage_, kc_)                                                                      \
@@ -383,8 +395,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 }  // namespace
 
 moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_perm_scale,
-                          const int32_t* offsets, const moe_expert_weights* w, const bf16_t* x,
-                          bf16_t* y_perm, bf16_t* y_shared, void* ws, int phase, hipStream_t st) {
+                          const int32_t* perm, const int32_t* offsets, const moe_expert_weights* w,
+                          const bf16_t* x, bf16_t* y_perm, bf16_t* y_shared, void* ws, int phase,
+                          hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
   const int32_t* hdr = reinterpret_cast<const int32_t*>(base + L.off_hdr);
@@ -397,10 +410,13 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
   constexpr int kThreads8 = 64 * kWM8 * kWN8;
   moe_status s;
   Fp8Params p{};
-  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
+  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
   if (phase == MOE_FFN_ALL || phase == MOE_FFN_GATE_UP) {
     if ((s = launch_build_tiles(c, offsets, ws, st)) != MOE_OK) return s;
-    if (c->S > 0 && (s = launch_quantize_rows(x, c->T, c->H, xq, xqs, st)) != MOE_OK) return s;
+    // x once in E4M3 (1 x 128 scales): the shared experts' operand, and the
+    // routed one when its rows are gathered
+    if ((c->S > 0 || perm) && (s = launch_quantize_rows(x, c->T, c->H, xq, xqs, st)) != MOE_OK) return s;
+    p.perm = perm;
     p.a_routed = x_perm; p.sa_routed = x_perm_scale;
     p.a_shared = xq; p.sa_shared = xqs;
     p.w_routed = (const fp8_t*)w->w_gate_up; p.sw_routed = w->w_gate_up_scale;
@@ -417,6 +433,7 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     }
   }
   if (phase == MOE_FFN_ALL || phase == MOE_FFN_DOWN) {
+    p.perm = nullptr;
     p.a_routed = hp; p.sa_routed = hps;
     p.a_shared = hs; p.sa_shared = hss;
     p.w_routed = (const fp8_t*)w->w_down; p.sw_routed = w->w_down_scale;

@@ -3,7 +3,9 @@
 MoeLayerGPU uploads a layer's weights once, allocates every buffer the calls
 need for T tokens, and runs route -> dispatch -> expert FFN -> combine ->
 bias update on the current stream.  It only allocates and marshals; every step
-of the layer runs in libmoe's kernels.
+of the layer runs in libmoe's kernels.  With gather=True, dispatch writes only
+the indices and the routed gate/up GEMM reads its rows from x through perm
+(moe_expert_ffn_gather); no x_perm is allocated.
 """
 from __future__ import annotations
 
@@ -24,9 +26,10 @@ def to_device(arr, device="cuda"):
 
 
 class MoeLayerGPU:
-    def __init__(self, cfg, weights, T=None, device="cuda"):
+    def __init__(self, cfg, weights, T=None, device="cuda", gather=False):
         self.c = cfg
         self.device = device
+        self.gather = gather
         self.fp8 = cfg.wgt == "fp8_e4m3"
         self.act_dtype = torch.float32 if cfg.act == "f32" else torch.bfloat16
         dev = lambda a: to_device(a, device)
@@ -71,7 +74,9 @@ class MoeLayerGPU:
         self.offsets = torch.empty(c.E + 1, dtype=i32, device=d)
         self.perm = torch.empty(P, dtype=i32, device=d)
         self.inv = torch.empty((T, c.k), dtype=i32, device=d)
-        if self.fp8:
+        if self.gather:
+            self.x_perm = self.x_perm_scale = None
+        elif self.fp8:
             self.x_perm = torch.empty((P, c.H), dtype=torch.uint8, device=d)
             self.x_perm_scale = torch.empty((P, c.H // 128), dtype=f32, device=d)
         else:
@@ -94,8 +99,12 @@ class MoeLayerGPU:
                        self.x_perm_scale, self.ws_dispatch)
 
     def expert_ffn(self, x, phase=L.MOE_FFN_ALL):
-        L.moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_scale, self.offsets, self.weights, x, self.y_perm,
-                         self.y_shared, self.ws_ffn, phase)
+        if self.gather:
+            L.moe_expert_ffn_gather(self.cfg, x, self.perm, self.offsets, self.weights, self.y_perm,
+                                    self.y_shared, self.ws_ffn, phase)
+        else:
+            L.moe_expert_ffn(self.cfg, self.x_perm, self.x_perm_scale, self.offsets, self.weights, x,
+                             self.y_perm, self.y_shared, self.ws_ffn, phase)
 
     def combine(self):
         L.moe_combine(self.cfg, self.y_perm, self.y_shared, self.inv, self.topk_w, self.y)

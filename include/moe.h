@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -121,7 +121,9 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
  *  perm      [T*k] int32 out: flat pair ids f = t*k + j, stably sorted by expert
  *  inv       [T, k] int32 out: row of pair (t, j) in the permuted order
  *  x_perm    [T*k, H] out: row p = x[perm[p] / k]; act dtype, or E4M3 bytes when
- *            wgt == FP8_E4M3 (quantised per 1x128 tile: sc = amax/448, q = e4m3(v/sc))
+ *            wgt == FP8_E4M3 (quantised per 1x128 tile: sc = amax/448, q = e4m3(v/sc)).
+ *            NULL: only counts, offsets, perm and inv are written (x and
+ *            x_perm_scale may then be NULL too), for moe_expert_ffn_gather.
  *  x_perm_scale [T*k, H/128] fp32 out (FP8 only, else NULL)
  *  ws, ws_bytes  workspace of at least moe_workspace_bytes(cfg, MOE_WS_DISPATCH)
  */
@@ -174,6 +176,28 @@ moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x
                           const int32_t* offsets, const moe_expert_weights* w, const void* x,
                           void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
                           void* stream);
+
+/*
+ * moe_expert_ffn_gather - moe_expert_ffn with dispatch's row copy folded into
+ * the routed gate/up GEMM: its operand row p is read straight from
+ * x[perm[p] / k] (same arithmetic, same order: y_perm and y_shared equal
+ * moe_expert_ffn's bit for bit).  For FP8 the kernel quantises x once per
+ * 1x128 tile into the workspace and gathers codes and scales from there (the
+ * same codes moe_dispatch would write into x_perm).
+ *
+ * Follows: the per-expert token rows of dispatch (DeepSeek-V3 Technical
+ * Report：中英对照解读, §2.2) read in place instead of copied.
+ *
+ *  x         [T, H] act dtype in (bf16 for FP8 weights)
+ *  perm, offsets  as written by moe_dispatch (which may then skip x_perm)
+ *  w, y_perm, y_shared, ws, ws_bytes, phase  as for moe_expert_ffn
+ * MOE_ERR_UNSUPPORTED when (T+1) * H * (bytes per element) exceeds 2^31 - 1
+ * (the gathered rows are addressed by 32-bit byte offsets; bf16/FP8 only).
+ */
+moe_status moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_t* perm,
+                                 const int32_t* offsets, const moe_expert_weights* w,
+                                 void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
+                                 int phase, void* stream);
 
 /*
  * moe_combine - y[t] = y_shared[t] + sum_j topk_w[t, j] * y_perm[inv[t, j]]

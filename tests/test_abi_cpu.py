@@ -21,7 +21,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
     for st in (0, -1, -2, -3, -4, -5):
         assert len(L.status_string(st)) >= 2
 
@@ -95,6 +95,24 @@ def test_fp8_needs_scales():
     assert L.lib().moe_quantize_fp8(1, 1, 128, 100, 128, 1, 1, None) == L.MOE_ERR_SHAPE
     assert L.lib().moe_quantize_fp8(1, 1, 100, 128, 128, 1, 1, None) == L.MOE_ERR_SHAPE
     assert L.lib().moe_quantize_fp8(1, 1, 128, 128, 64, 1, 1, None) == L.MOE_ERR_UNSUPPORTED
+
+
+def test_gather_ffn_validation():
+    """moe_expert_ffn_gather: perm and x required, 32-bit row offsets into x checked."""
+    cfg = _cfg()
+    w = L.MoeExpertWeights(1, 1, None, None, 1, 1, None, None)
+    big = 1 << 40
+    fn = L.lib().moe_expert_ffn_gather
+    assert fn(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, big, 0, None) == L.MOE_ERR_NULL
+    assert fn(ctypes.byref(cfg), None, 1, 1, ctypes.byref(w), 1, 1, 1, big, 0, None) == L.MOE_ERR_NULL
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN)
+    assert fn(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), 1, 1, 1, need - 1, 0, None) == L.MOE_ERR_WORKSPACE
+    # (T + 1) * H * 2 bytes past 2^31 - 1: H = 2048 bf16 allows T <= 524286
+    assert fn(ctypes.byref(_cfg(T=524288)), 1, 1, 1, ctypes.byref(w), 1, 1, 1, big, 0, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    # moe_dispatch: x_perm needs x; x may be NULL only without x_perm
+    st = L.lib().moe_dispatch(ctypes.byref(cfg), 1, None, 1, 1, 1, 1, 1, None, 1, big, None)
+    assert st == L.MOE_ERR_NULL
 
 
 def test_workspace_sizes_scale_with_tokens():

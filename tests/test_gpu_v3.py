@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from biased_top_routing_amd import _lib as L
 from biased_top_routing_amd.runner import MoeLayerGPU, to_device
 from gpu_util import dev_f32, host, rel_inf, say
 from workloads import V3_PREFILL
@@ -113,3 +114,25 @@ def test_v3_decode_full_size(v3):
     xh, bias_h, bias_next, y = _run(c, w, layer, c.T, 3)
     s_ora, idx, offsets, perm = _check_routing(c, c.T, w, layer, xh, bias_h, bias_next)
     _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok=6, experts=(int(idx[0, 0]),))
+
+
+def test_v3_prefill_gather_bit_exact(v3):
+    """Dispatch without the row copy and the gate/up GEMM gathering its rows from x
+    (the benchmark's path) give the materialised path's indices and outputs bit for bit."""
+    w, layer = v3
+    c = V3_PREFILL
+    xh, _, _, _ = _run(c, w, layer, c.T, 0)
+    x = to_device(xh)
+    counts, offsets = torch.empty_like(layer.counts), torch.empty_like(layer.offsets)
+    perm, inv = torch.empty_like(layer.perm), torch.empty_like(layer.inv)
+    say("v3: dispatch without x_perm")
+    L.moe_dispatch(layer.cfg, layer.topk_idx, None, counts, offsets, perm, inv, None, None, layer.ws_dispatch)
+    for a, b in ((counts, layer.counts), (offsets, layer.offsets), (perm, layer.perm), (inv, layer.inv)):
+        assert torch.equal(a, b)
+    y_perm, y_shared = torch.empty_like(layer.y_perm), torch.empty_like(layer.y_shared)
+    ws = torch.empty_like(layer.ws_ffn)
+    say("v3: gathered expert FFN")
+    L.moe_expert_ffn_gather(layer.cfg, x, perm, offsets, layer.weights, y_perm, y_shared, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y_perm.view(torch.int16), layer.y_perm.view(torch.int16))
+    assert torch.equal(y_shared.view(torch.int16), layer.y_shared.view(torch.int16))
