@@ -12,9 +12,11 @@ that is the arithmetic the GPU must reproduce bit for bit.
 
 Pins: every function is checked in tests/ against something other than itself
 (brute-force enumeration, closed forms, library routines on special cases,
-hand-derived fixtures in tests/golden/).  Parity unpinned by the pages: the
-group-score rule (sum of the top-r biased scores of a group) and the balance
-trajectory values; both are readings, not page facts.
+hand-derived fixtures in tests/golden/, central finite differences of an
+independent forward for every gradient).  Parity unpinned by the pages: the
+group-score rule (sum of the top-r biased scores of a group), the balance
+trajectory values and the form of the sequence-wise balance loss; all are
+readings, not page facts.
 """
 from .route import affinity, route, route_diagnostics  # noqa: F401
 from .dispatch import dispatch, permute_rows  # noqa: F401
@@ -23,3 +25,4 @@ from .combine import combine  # noqa: F401
 from .balance import update_bias  # noqa: F401
 from .fp8 import e4m3_decode, e4m3_encode, quantize_rows_1x128, quantize_blocks_128x128, fp8_matmul  # noqa: F401
 from .layer import decode_act, forward_from_routing, layer_forward, sampled_forward  # noqa: F401
+from .backward import backward_from_routing, gate_backward, seq_balance_loss, swiglu_backward  # noqa: F401
