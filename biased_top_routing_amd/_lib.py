@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORES_IN = 1
 MOE_FFN_ALL, MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1, 2
-MOE_WS_DISPATCH, MOE_WS_FFN = 1, 2
+MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_FFN_BWD, MOE_WS_ROUTE_BWD = 1, 2, 3, 4
 MOE_WSP_H, MOE_WSP_H_SCALE, MOE_WSP_H_SHARED, MOE_WSP_H_SHARED_SCALE = 0, 1, 2, 3
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 
@@ -42,6 +42,10 @@ class MoeExpertWeights(ctypes.Structure):
         "ws_gate_up", "ws_down", "ws_gate_up_scale", "ws_down_scale")]
 
 
+class MoeExpertGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate_up", "w_down", "ws_gate_up", "ws_down")]
+
+
 _lib = None
 
 
@@ -62,6 +66,11 @@ def lib() -> ctypes.CDLL:
             "moe_expert_ffn_gather": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, sz,
                                       ctypes.c_int, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp],
+            "moe_combine_backward": [cfgp, vp, vp, vp, vp, vp, vp, vp],
+            "moe_expert_ffn_backward": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp,
+                                        ctypes.POINTER(MoeExpertGrads), vp, sz, vp],
+            "moe_route_backward": [cfgp, vp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, sz, vp],
+            "moe_dispatch_backward": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_update_bias": [cfgp, vp, vp, f32, vp],
             "moe_quantize_fp8": [vp, i32, i32, i32, i32, vp, vp, vp],
             "moe_ffn_workspace_part": [cfgp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz)],
@@ -164,6 +173,34 @@ def moe_expert_ffn_gather(cfg, x, perm, offsets, weights: MoeExpertWeights, y_pe
 def moe_combine(cfg, y_perm, y_shared, inv, topk_w, y, stream=None):
     _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _p(y_perm), _p(y_shared), _p(inv), _p(topk_w),
                                             _p(y), _s(stream)))
+
+
+def expert_grads(w_gate_up, w_down, ws_gate_up=None, ws_down=None) -> MoeExpertGrads:
+    return MoeExpertGrads(_p(w_gate_up), _p(w_down), _p(ws_gate_up), _p(ws_down))
+
+
+def moe_combine_backward(cfg, dy, y_perm, inv, topk_w, dy_perm, d_topk_w, stream=None):
+    _check("moe_combine_backward", lib().moe_combine_backward(
+        ctypes.byref(cfg), _p(dy), _p(y_perm), _p(inv), _p(topk_w), _p(dy_perm), _p(d_topk_w), _s(stream)))
+
+
+def moe_expert_ffn_backward(cfg, x_perm, x, offsets, weights: MoeExpertWeights, dy_perm, dy, dx_perm, dx_shared,
+                            grads: MoeExpertGrads, ws, stream=None):
+    _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
+        ctypes.byref(cfg), _p(x_perm), _p(x), _p(offsets), ctypes.byref(weights), _p(dy_perm), _p(dy), _p(dx_perm),
+        _p(dx_shared), ctypes.byref(grads), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moe_route_backward(cfg, x, w_router, scores, topk_idx, d_topk_w, alpha, seq_len, dx_router, dw_router, loss, ws,
+                       stream=None):
+    _check("moe_route_backward", lib().moe_route_backward(
+        ctypes.byref(cfg), _p(x), _p(w_router), _p(scores), _p(topk_idx), _p(d_topk_w), float(alpha), int(seq_len),
+        _p(dx_router), _p(dw_router), _p(loss), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moe_dispatch_backward(cfg, dx_perm, dx_shared, dx_router, inv, dx, stream=None):
+    _check("moe_dispatch_backward", lib().moe_dispatch_backward(
+        ctypes.byref(cfg), _p(dx_perm), _p(dx_shared), _p(dx_router), _p(inv), _p(dx), _s(stream)))
 
 
 def moe_update_bias(cfg, counts, bias, gamma, stream=None):

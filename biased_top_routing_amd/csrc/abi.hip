@@ -1,6 +1,7 @@
 // Host side of the C ABI: configuration checks, workspace sizing, status text.
 // Everything here runs before any device call, so it also works without a GPU.
 #include "common.h"
+#include "bwd_layout.h"
 #include "ffn_layout.h"
 
 namespace moe {
@@ -50,6 +51,8 @@ extern "C" size_t moe_workspace_bytes(const moe_cfg* cfg, int which) {
   if (validate_cfg(cfg) != MOE_OK) return 0;
   if (which == MOE_WS_DISPATCH) return dispatch_ws_bytes(cfg);
   if (which == MOE_WS_FFN) return FfnLayout(cfg).total;
+  if (which == MOE_WS_FFN_BWD) return FfnBwdLayout(cfg).total;
+  if (which == MOE_WS_ROUTE_BWD) return RouteBwdLayout(cfg, 0).total;
   return 0;
 }
 

@@ -1,0 +1,85 @@
+// Workspace layouts of the backward calls (host and device agree on them).
+#pragma once
+
+#include "common.h"
+#include "ffn_layout.h"
+
+namespace moe {
+
+// Backward GEMM tiles: 256 x 256 outputs, K slices of 64.
+constexpr int kBwdBM = 256, kBwdBN = 256;
+
+// moe_expert_ffn_backward: tile tables of the three row-segmented GEMMs (gate/up
+// recomputation, dh, dx), the recomputed gate and up outputs g, u, the gradient
+// of the gate/up outputs dgu (gate part, then up part, per expert), and h
+// recomputed for the down weights' gradient.  Routed rows [T*k, .], shared
+// rows [T, S * .]; all bf16.
+struct FfnBwdLayout {
+  int64_t P;
+  int64_t max_re, max_dh, max_dx;                  // tile-table capacities
+  int nt_re, nts_re, nt_dh, nts_dh, nt_dx;         // column tiles
+  size_t off_hdr, off_tre, off_tdh, off_tdx;
+  size_t off_g, off_u, off_gs, off_us, off_dgu, off_dgus, off_h, off_hs, total;
+
+  explicit FfnBwdLayout(const moe_cfg* c) {
+    P = pairs(c);
+    const int64_t SI = (int64_t)c->S * c->I;
+    nt_re = (c->I + kBNH - 1) / kBNH;
+    nts_re = (int)((SI + kBNH - 1) / kBNH);
+    nt_dh = (c->I + kBwdBN - 1) / kBwdBN;
+    nts_dh = (int)((SI + kBwdBN - 1) / kBwdBN);
+    nt_dx = (c->H + kBwdBN - 1) / kBwdBN;
+    const int64_t rs_re = c->S > 0 ? (c->T + kBM1 - 1) / kBM1 : 0;
+    const int64_t rs_bw = c->S > 0 ? (c->T + kBwdBM - 1) / kBwdBM : 0;
+    max_re = (P / kBM1 + c->E) * nt_re + rs_re * nts_re;
+    max_dh = (P / kBwdBM + c->E) * nt_dh + rs_bw * nts_dh;
+    max_dx = (P / kBwdBM + c->E + rs_bw) * nt_dx;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+    off_hdr = take(64);
+    off_tre = take((size_t)max_re * sizeof(TileDesc));
+    off_tdh = take((size_t)max_dh * sizeof(TileDesc));
+    off_tdx = take((size_t)max_dx * sizeof(TileDesc));
+    off_g = take((size_t)P * c->I * 2);
+    off_u = take((size_t)P * c->I * 2);
+    off_gs = take((size_t)c->T * SI * 2);
+    off_us = take((size_t)c->T * SI * 2);
+    off_dgu = take((size_t)P * 2 * c->I * 2);
+    off_dgus = take((size_t)c->T * 2 * SI * 2);
+    off_h = take((size_t)P * c->I * 2);
+    off_hs = take((size_t)c->T * SI * 2);
+    total = o;
+  }
+};
+
+// moe_route_backward: per-chunk expert statistics of every sequence (selection
+// counts and sums of the normalised affinities), the per-(sequence, expert)
+// coefficient of the balance loss, dlogit in bf16 for the GEMMs, and the
+// split-K partial sums of the router weights' gradient.
+constexpr int kSeqChunk = 64;      // tokens per statistics chunk
+constexpr int kRouterKSplit = 1024;  // token rows per split of the router-weight gradient
+
+struct RouteBwdLayout {
+  int nseq, seq_len, nchunk, nsplit;
+  size_t off_cnt, off_psum, off_coef, off_dlogit, off_part, total;
+
+  RouteBwdLayout(const moe_cfg* c, int seq) {
+    seq_len = seq > 0 ? seq : (c->T > 0 ? c->T : 1);
+    nseq = c->T / seq_len;
+    nchunk = (seq_len + kSeqChunk - 1) / kSeqChunk;
+    nsplit = (c->T + kRouterKSplit - 1) / kRouterKSplit;
+    // sizes from bounds that hold for every sequence length (nseq * nchunk <=
+    // T + T / 64 + 1, nseq <= T), so the workspace size does not depend on it
+    const size_t chunks_max = (size_t)c->T + c->T / kSeqChunk + 1, seqs_max = (size_t)(c->T > 0 ? c->T : 1);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes, 256); return at; };
+    off_cnt = take(chunks_max * c->E * 4);
+    off_psum = take(chunks_max * c->E * 4);
+    off_coef = take(seqs_max * c->E * 4);
+    off_dlogit = take((size_t)c->T * c->E * 2);
+    off_part = take((size_t)nsplit * c->E * c->H * 4);
+    total = o;
+  }
+};
+
+}  // namespace moe

@@ -66,9 +66,9 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   __syncthreads();
   if (tid == 0 && blockIdx.x == 0) {
     hdr[0] = total1;
-    hdr[1] = total2;
+    hdr[1] = t2 ? total2 : 0;
   }
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < (t2 ? 2 : 1); ++pass) {   // t2 == nullptr: the first table only
     const int* pre = pass == 0 ? pre1 : pre2;
     const int total = pass == 0 ? total1 : total2;
     TileDesc* out = pass == 0 ? t1 : t2;
@@ -100,17 +100,23 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
   }
 }
 
+moe_status launch_build_tile_tables(const moe_cfg* c, const int32_t* offsets, int bm1, int nt1, int nt1s,
+                                    TileDesc* t1, int64_t max1, int bm2, int nt2, TileDesc* t2, int64_t max2,
+                                    int32_t* hdr, hipStream_t st) {
+  const int64_t most = max1 > max2 ? max1 : max2;
+  const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((most + 1023) / 1024, 1), 64);
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(blocks), dim3(1024), 0, st, offsets, c->E, c->S, c->T, bm1, bm2, nt1,
+                     nt1s, nt2, t1, t2, hdr);
+  return launch_status();
+}
+
 moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws, hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
-  const int64_t most = L.max1 > L.max2 ? L.max1 : L.max2;
-  const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((most + 1023) / 1024, 1), 64);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(blocks), dim3(1024), 0, st, offsets, c->E, c->S, c->T, L.bm1, L.bm2,
-                     (int)L.nt1, (int)L.nt1s, (int)L.nt2,
-                     reinterpret_cast<TileDesc*>(base + L.off_t1),
-                     reinterpret_cast<TileDesc*>(base + L.off_t2),
-                     reinterpret_cast<int32_t*>(base + L.off_hdr));
-  return launch_status();
+  return launch_build_tile_tables(c, offsets, L.bm1, (int)L.nt1, (int)L.nt1s,
+                                  reinterpret_cast<TileDesc*>(base + L.off_t1), L.max1, L.bm2, (int)L.nt2,
+                                  reinterpret_cast<TileDesc*>(base + L.off_t2), L.max2,
+                                  reinterpret_cast<int32_t*>(base + L.off_hdr), st);
 }
 
 // ------------------------------------------------------------ fp32 experts

@@ -21,14 +21,15 @@
 // (workgroup id mod 8), so tiles sharing operands run together in one XCD's L2.
 #include "common.h"
 #include "ffn_layout.h"
+#include "gemm_common.h"
 #include "kernels.h"
 
 namespace moe {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-enum { kRouter = 0, kGateUp = 1, kDown = 2 };
+// kGateUpGU: the gate/up GEMM storing the gate and up outputs themselves
+// (recomputed for the backward pass) instead of h.
+enum { kRouter = 0, kGateUp = 1, kDown = 2, kGateUpGU = 3 };
+constexpr bool is_gate_up(int mode) { return mode == kGateUp || mode == kGateUpGU; }
 
 
 struct GemmParams {
@@ -37,58 +38,15 @@ struct GemmParams {
   const bf16_t* w_routed;   // gate/up: w_gate_up; down: w_down; router: w_router
   const bf16_t* w_shared;   // gate/up: ws_gate_up; down: ws_down
   const float* offset;      // router logit offset (nullable)
-  void* out_routed;         // gate/up: h_perm; down: y_perm; router: scores (fp32)
-  void* out_shared;         // gate/up: h_shared; down: y_shared
+  void* out_routed;         // gate/up: h_perm; down: y_perm; router: scores (fp32); gate/up GU: gate
+  void* out_shared;         // gate/up: h_shared; down: y_shared; gate/up GU: gate
+  void* out2_routed;        // gate/up GU: up outputs
+  void* out2_shared;
   const TileDesc* tiles;
   const int32_t* ntiles;
   const int32_t* perm;      // gate/up: non-null -> routed rows gathered from a_shared
   int T, H, E, S, I, k;
 };
-
-// s_waitcnt immediate that waits until at most N vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left at their maxima; gfx9
-// encoding: vmcnt in bits 3:0 and 15:14).
-template <int N>
-constexpr int kVmWaitOneStage() {
-  return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
-}
-
-// Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
-constexpr int kBufferWord3 = 0x00020000;
-
-// Raw buffer descriptor over [base, base + bytes), built from wave-uniform
-// values so that it lives in SGPRs.
-#if defined(__HIP_DEVICE_COMPILE__)   // the descriptor type exists only for the GPU target
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ub, 0, __builtin_amdgcn_readfirstlane(bytes), kBufferWord3);
-}
-#endif
-
-// Physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per row).
-template <int CPR>
-__device__ __forceinline__ int swz(int r, int c) {
-  if constexpr (CPR == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
-  else return c ^ (((r >> 1) ^ (r >> 2)) & 3);   // CPR == 4
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_s_waitcnt(kVmWaitOneStage<N>());
-}
-
-// Waits until at most `n` slices' loads (PER instructions each) of this wave
-// are outstanding; n < 4.
-template <int PER>
-__device__ __forceinline__ void wait_slices(int n) {
-  if (n <= 0) wait_vm<0>();
-  else if (n == 1) wait_vm<PER>();
-  else if (n == 2) wait_vm<2 * PER>();
-  else wait_vm<3 * PER>();
-}
 
 // Tile of (WM*MI*32) token rows x (WN*NI*32) weight rows; wave (wm, wn) owns
 // MI x NI MFMA 32x32 blocks.  K advances BK columns per slice through a ring of
@@ -136,7 +94,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   // Routed gate/up rows gathered straight from x: row row0 + r of the
   // expert-sorted order is token perm[row0 + r] / k (dispatch's row copy
   // folded into the operand loads).
-  const bool gather = MODE == kGateUp && !shared && p.perm != nullptr;
+  const bool gather = is_gate_up(MODE) && !shared && p.perm != nullptr;
 
   // ------------------------------------------------------------ operand bases
   const bf16_t* A;
@@ -160,7 +118,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     W = p.w_routed;
     ldw = p.H;
     ncols = p.E;
-  } else if constexpr (MODE == kGateUp) {
+  } else if constexpr (is_gate_up(MODE)) {
     W = shared ? p.w_shared : p.w_routed + (int64_t)seg * 2 * p.I * p.H;
     ldw = p.H;
     ncols = shared ? p.S * p.I : p.I;
@@ -183,7 +141,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   for (int i = 0; i < A_CH; ++i) {
     const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int src = r < rows ? r : a_rows + 1;
-    if constexpr (MODE == kGateUp)
+    if constexpr (is_gate_up(MODE))
       if (gather && r < rows) src = p.perm[row0 + r] / p.k;
     a_off[i] = src * lda + swz<CPR>(r, pc) * 8;
   }
@@ -191,7 +149,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   for (int i = 0; i < B_CH; ++i) {
     const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
     int wrow;
-    if constexpr (MODE == kGateUp) {
+    if constexpr (is_gate_up(MODE)) {
       // rows [0, BN/2) gate, [BN/2, BN) up, of h columns nt*BN/2 + j
       const bool up = r >= BN / 2;
       const int c = min(nt * (BN / 2) + (up ? r - BN / 2 : r), ncols - 1);
@@ -207,7 +165,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   // (the host checks that a segment's weights stay below 2 GiB)
   int w_bytes;
   if constexpr (MODE == kRouter) w_bytes = p.E * p.H * 2;
-  else if constexpr (MODE == kGateUp) w_bytes = (shared ? p.S : 1) * 2 * p.I * p.H * 2;
+  else if constexpr (is_gate_up(MODE)) w_bytes = (shared ? p.S : 1) * 2 * p.I * p.H * 2;
   else w_bytes = (shared ? p.S : 1) * p.H * p.I * 2;
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, a_rows * lda * 2);
   const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(W, w_bytes);
@@ -250,7 +208,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni) {
     int brow;
-    if constexpr (MODE == kGateUp) {
+    if constexpr (is_gate_up(MODE)) {
       constexpr int HALF = NI / 2;   // gate blocks, then the matching up blocks
       brow = (ni < HALF ? 0 : BN / 2) + wn * HALF * 32 + (ni % HALF) * 32;
     } else {
@@ -341,6 +299,18 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
           const float h = g / (1.0f + __expf(-g)) * u;
           if (col < ncols) out[row * ncols + col] = f32_to_bf16(h);
         }
+      } else if constexpr (MODE == kGateUpGU) {
+        constexpr int HALF = NI / 2;
+        bf16_t* og = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+        bf16_t* ou = static_cast<bf16_t*>(shared ? p.out2_shared : p.out2_routed);
+#pragma unroll
+        for (int ni = 0; ni < HALF; ++ni) {
+          const int col = nt * (BN / 2) + wn * HALF * 32 + ni * 32 + lr;
+          if (col < ncols) {
+            og[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
+            ou[row * ncols + col] = f32_to_bf16(acc[mi][ni + HALF][r]);
+          }
+        }
       } else if constexpr (MODE == kDown) {
         bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
 #pragma unroll
@@ -428,6 +398,25 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     }
   }
   return MOE_OK;
+}
+
+moe_status launch_gateup_recompute_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf16_t* x,
+                                        const moe_expert_weights* w, const TileDesc* tiles,
+                                        const int32_t* ntiles, int64_t max_tiles, bf16_t* g, bf16_t* u,
+                                        bf16_t* gs, bf16_t* us, hipStream_t st) {
+  GemmParams p{};
+  p.a_routed = x_perm; p.a_shared = x;
+  p.w_routed = (const bf16_t*)w->w_gate_up; p.w_shared = (const bf16_t*)w->ws_gate_up;
+  p.out_routed = g; p.out2_routed = u;
+  p.out_shared = gs; p.out2_shared = us;
+  p.tiles = tiles;
+  p.ntiles = ntiles;
+  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
+  const int64_t grid = align_up((size_t)max_tiles, 8);
+  if (grid > 0)
+    hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpGU, MOE_GU_TILE>), dim3((unsigned)grid),
+                       dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
+  return launch_status();
 }
 
 }  // namespace moe

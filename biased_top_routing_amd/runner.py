@@ -112,6 +112,46 @@ class MoeLayerGPU:
     def update_bias(self, bias, gamma):
         L.moe_update_bias(self.cfg, self.counts, bias, gamma)
 
+    # ---------------------------------------------------------------- backward
+    def alloc_backward(self):
+        """Gradient buffers for the current T (fp32 weight gradients, bf16 activation gradients)."""
+        c, d = self.c, self.device
+        T, P = self.T, self.T * c.k
+        bf, f32 = torch.bfloat16, torch.float32
+        self.dy_perm = torch.empty((P, c.H), dtype=bf, device=d)
+        self.d_topk_w = torch.empty((T, c.k), dtype=f32, device=d)
+        self.dx_perm = torch.empty((P, c.H), dtype=bf, device=d)
+        self.dx_shared = torch.empty((T, c.H), dtype=bf, device=d) if c.S > 0 else None
+        self.dx_router = torch.empty((T, c.H), dtype=f32, device=d)
+        self.dx = torch.empty((T, c.H), dtype=bf, device=d)
+        self.g_w_gate_up = torch.empty((c.E, 2 * c.I, c.H), dtype=f32, device=d)
+        self.g_w_down = torch.empty((c.E, c.H, c.I), dtype=f32, device=d)
+        self.g_ws_gate_up = torch.empty((c.S, 2 * c.I, c.H), dtype=f32, device=d) if c.S > 0 else None
+        self.g_ws_down = torch.empty((c.S, c.H, c.I), dtype=f32, device=d) if c.S > 0 else None
+        self.g_w_router = torch.empty((c.E, c.H), dtype=f32, device=d)
+        self.loss_bal = torch.empty(1, dtype=f32, device=d)
+        self.grads = L.expert_grads(self.g_w_gate_up, self.g_w_down, self.g_ws_gate_up, self.g_ws_down)
+        self.ws_ffn_bwd = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_FFN_BWD), dtype=torch.uint8, device=d)
+        self.ws_route_bwd = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_ROUTE_BWD), dtype=torch.uint8,
+                                        device=d)
+        self._bwd_T = T
+
+    def backward(self, x, dy, alpha=0.0, seq_len=0):
+        """Gradients of sum(dy * y) + alpha-weighted sequence balance loss for the last forward pass
+        (same x, same routing).  Fills dx, the fp32 weight gradients and loss_bal; returns dx."""
+        if self.gather:
+            raise ValueError("backward reads the permuted rows x_perm: build the layer with gather=False")
+        if getattr(self, "_bwd_T", None) != self.T:
+            self.alloc_backward()
+        cfg = self.cfg
+        L.moe_combine_backward(cfg, dy, self.y_perm, self.inv, self.topk_w, self.dy_perm, self.d_topk_w)
+        L.moe_expert_ffn_backward(cfg, self.x_perm, x, self.offsets, self.weights, self.dy_perm, dy, self.dx_perm,
+                                  self.dx_shared, self.grads, self.ws_ffn_bwd)
+        L.moe_route_backward(cfg, x, self.w_router, self.scores, self.topk_idx, self.d_topk_w, alpha, seq_len,
+                             self.dx_router, self.g_w_router, self.loss_bal, self.ws_route_bwd)
+        L.moe_dispatch_backward(cfg, self.dx_perm, self.dx_shared, self.dx_router, self.inv, self.dx)
+        return self.dx
+
     def forward(self, x, bias, gamma=None, scores_in=False):
         """One batch through the layer; with gamma set, bias is updated in place afterwards."""
         self.route(x, bias, scores_in)

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -233,9 +233,97 @@ moe_status moe_update_bias(const moe_cfg* cfg, const int32_t* counts, float* bia
 moe_status moe_quantize_fp8(const void* src_bf16, int32_t n_mat, int32_t rows, int32_t cols,
                             int32_t block_rows, uint8_t* dst, float* scales, void* stream);
 
+/* ------------------------------------------------------------------ backward
+ * The gradient of one layer pass (the training step the bias rule lives in),
+ * for act = wgt = BF16 (other dtypes: MOE_ERR_UNSUPPORTED).  With the expert
+ * choice of the forward pass fixed, the loss sum(dy * y) + L_bal is
+ * differentiated exactly: the expert choice and the bias carry no gradient
+ * (the bias only ranks experts; the gates come from the raw affinities:
+ * reading notes on the DeepSeek-V3 report, Method §1).  Order of the calls:
+ *   moe_combine_backward -> moe_expert_ffn_backward -> moe_route_backward ->
+ *   moe_dispatch_backward
+ * Gradients of activations are bf16 with fp32 accumulation inside every
+ * kernel; weight gradients are fp32 (the pages keep gradients in high
+ * precision: qwbw.cn essay, FP8 part of the infrastructure section).
+ */
+
+/*
+ * moe_combine_backward - gradients of y[t] = y_shared[t] + sum_j w[t,j] y_perm[inv[t,j]]:
+ *   d_topk_w[t,j]       = sum_h dy[t,h] * y_perm[inv[t,j],h]   (fp32)
+ *   dy_perm[inv[t,j],:] = topk_w[t,j] * dy[t,:]                 (bf16)
+ * (the shared experts' output gradient is dy itself).
+ *  dy [T, H], y_perm [T*k, H] (as written by moe_expert_ffn), inv, topk_w [T, k];
+ *  dy_perm [T*k, H] out; d_topk_w [T, k] fp32 out.
+ */
+moe_status moe_combine_backward(const moe_cfg* cfg, const void* dy, const void* y_perm, const int32_t* inv,
+                                const float* topk_w, void* dy_perm, float* d_topk_w, void* stream);
+
+/* Weight gradients (fp32, the weights' shapes). */
+typedef struct {
+  float* w_gate_up;   /* [E, 2I, H] */
+  float* w_down;      /* [E, H, I] */
+  float* ws_gate_up;  /* [S, 2I, H] (S > 0) */
+  float* ws_down;     /* [S, H, I] (S > 0) */
+} moe_expert_grads;
+
+/*
+ * moe_expert_ffn_backward - gradients of the routed experts on their segments
+ * and of the shared experts on every token.  Recomputes the gate and up
+ * outputs g, u (the forward pass keeps only h), then per expert
+ *   dh = dY W_d;  dg = dh * u * silu'(g);  du = dh * silu(g);  h = silu(g) * u
+ *   dX = [dg du] W_gu;  dW_gu = [dg du]^T X;  dW_d = dY^T h
+ * with dY = dy_perm (routed rows) or dy (shared), X = x_perm or x
+ * (SwiGLU experts: DeepSeek-V3 Technical Report：中英对照解读, §2).
+ *  x_perm [T*k, H] (moe_dispatch's permuted rows), x [T, H], offsets as written
+ *  by moe_dispatch; w the forward weights; dy_perm [T*k, H] from
+ *  moe_combine_backward; dy [T, H];
+ *  dx_perm [T*k, H] out (routed rows' input gradient, permuted order);
+ *  dx_shared [T, H] out (S > 0); grads out (every member non-NULL; the shared
+ *  ones when S > 0); ws of at least moe_workspace_bytes(cfg, MOE_WS_FFN_BWD).
+ * MOE_ERR_UNSUPPORTED when T * max(H, 2 * max(S, 1) * I) * 2 bytes exceeds
+ * 2^31 - 1 (operand rows are addressed by 32-bit offsets within a segment).
+ */
+moe_status moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const void* x,
+                                   const int32_t* offsets, const moe_expert_weights* w, const void* dy_perm,
+                                   const void* dy, void* dx_perm, void* dx_shared, const moe_expert_grads* grads,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_route_backward - gradients through the gates and the router, plus the
+ * sequence-wise balance loss.
+ *   gates   w_j = scale * s_j / sum_j' s_j' over the selected experts:
+ *           ds_j = (scale / S) (dw_j - sum_j' dw_j' s_j' / S),  S = sum_j s_j
+ *   balance (reading; the pages keep a sequence-wise balance loss with a very
+ *           small weight alpha but print no formula: reading notes, Method §1):
+ *           sequences of seq_len consecutive tokens; per sequence
+ *           f_e = E / (k L) * (selections of e), P_e = mean_t s_te / sum_e' s_te',
+ *           L_bal = alpha * mean over sequences of sum_e f_e P_e
+ *   router  dlogit = ds * s (1 - s);  dx_router = dlogit W_r;  dw_router = dlogit^T x
+ *  x [T, H], w_router [E, H] bf16; scores [T, E] fp32 affinities (moe_route's
+ *  output); topk_idx [T, k]; d_topk_w [T, k] from moe_combine_backward;
+ *  alpha >= 0 (0: no balance loss); seq_len 0 (= T) or a divisor of T;
+ *  dx_router [T, H] fp32 out (may be NULL); dw_router [E, H] fp32 out;
+ *  loss: one fp32 out (L_bal); ws of at least moe_workspace_bytes(cfg, MOE_WS_ROUTE_BWD).
+ */
+moe_status moe_route_backward(const moe_cfg* cfg, const void* x, const void* w_router, const float* scores,
+                              const int32_t* topk_idx, const float* d_topk_w, float alpha, int32_t seq_len,
+                              float* dx_router, float* dw_router, float* loss, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * moe_dispatch_backward - the input gradient of the layer:
+ *   dx[t] = sum_j dx_perm[inv[t,j]] + dx_shared[t] + dx_router[t]
+ * accumulated in fp32 (slots in order, then the shared and router terms), dx
+ * bf16.  dx_shared may be NULL when S == 0, dx_router may be NULL.
+ */
+moe_status moe_dispatch_backward(const moe_cfg* cfg, const void* dx_perm, const void* dx_shared,
+                                 const float* dx_router, const int32_t* inv, void* dx, void* stream);
+
 /* Workspace kinds for moe_workspace_bytes */
 #define MOE_WS_DISPATCH 1
 #define MOE_WS_FFN 2
+#define MOE_WS_FFN_BWD 3
+#define MOE_WS_ROUTE_BWD 4
 
 /* Bytes of workspace a call needs for this configuration (0 on an invalid cfg). */
 size_t moe_workspace_bytes(const moe_cfg* cfg, int which);

@@ -21,7 +21,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
     for st in (0, -1, -2, -3, -4, -5):
         assert len(L.status_string(st)) >= 2
 
@@ -113,6 +113,39 @@ def test_gather_ffn_validation():
     # moe_dispatch: x_perm needs x; x may be NULL only without x_perm
     st = L.lib().moe_dispatch(ctypes.byref(cfg), 1, None, 1, 1, 1, 1, 1, None, 1, big, None)
     assert st == L.MOE_ERR_NULL
+
+
+def test_backward_validation():
+    """The backward calls: bf16 only, NULL checks, alpha and seq_len, workspace sizes, offset limits."""
+    cfg = _cfg()
+    big = 1 << 40
+    lb = L.lib()
+    w = L.MoeExpertWeights(1, 1, None, None, 1, 1, None, None)
+    g = L.MoeExpertGrads(1, 1, 1, 1)
+    for bad in (L.cfg_from(V3_FP8), L.cfg_from(TINY)):       # FP8 and fp32 layers: not supported
+        assert lb.moe_combine_backward(ctypes.byref(bad), 1, 1, 1, 1, 1, 1, None) == L.MOE_ERR_UNSUPPORTED
+        assert lb.moe_dispatch_backward(ctypes.byref(bad), 1, 1, 1, 1, 1, None) == L.MOE_ERR_UNSUPPORTED
+    assert lb.moe_combine_backward(ctypes.byref(cfg), 1, None, 1, 1, 1, 1, None) == L.MOE_ERR_NULL
+    assert lb.moe_dispatch_backward(ctypes.byref(cfg), 1, None, None, 1, 1, None) == L.MOE_ERR_NULL   # S > 0
+    ffn = lb.moe_expert_ffn_backward
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN_BWD)
+    assert need > L.moe_workspace_bytes(cfg, L.MOE_WS_FFN)
+    assert ffn(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), 1, 1, 1, 1, ctypes.byref(g), 1, need - 1, None) \
+        == L.MOE_ERR_WORKSPACE
+    g0 = L.MoeExpertGrads(1, 1, None, 1)
+    assert ffn(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), 1, 1, 1, 1, ctypes.byref(g0), 1, big, None) \
+        == L.MOE_ERR_NULL
+    assert ffn(ctypes.byref(_cfg(T=1 << 20)), 1, 1, 1, ctypes.byref(w), 1, 1, 1, 1, ctypes.byref(g), 1, big,
+               None) == L.MOE_ERR_UNSUPPORTED             # T * 2 * S * I * 2 bytes past 2^31
+    rb = lb.moe_route_backward
+    need_r = L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE_BWD)
+    args = lambda alpha, seq, ws: (ctypes.byref(cfg), 1, 1, 1, 1, 1, alpha, seq, 1, 1, 1, 1, ws, None)
+    assert rb(*args(-1.0, 0, big)) == L.MOE_ERR_SHAPE
+    assert rb(*args(float("nan"), 0, big)) == L.MOE_ERR_SHAPE
+    assert rb(*args(0.1, 3, big)) == L.MOE_ERR_SHAPE       # T = 4096 is no multiple of 3
+    assert rb(*args(0.1, -4, big)) == L.MOE_ERR_SHAPE
+    assert rb(*args(0.1, 1024, need_r - 1)) == L.MOE_ERR_WORKSPACE
+    assert rb(ctypes.byref(cfg), 1, 1, 1, 1, 1, 0.0, 0, 1, None, 1, 1, big, None) == L.MOE_ERR_NULL
 
 
 def test_workspace_sizes_scale_with_tokens():
