@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the decode-size and FP8 measurements that follow the headline one")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="rough budget of the CPU oracle sample")
+    ap.add_argument("--train-only", action="store_true",
+                    help="diagnostic: time only the training step (forward + backward) and print its JSON")
     ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
                     help="gather: dispatch writes the indices and the gate/up GEMM reads its rows from x "
                          "through perm; copy: dispatch also writes x_perm and the GEMM reads that")
@@ -203,11 +205,88 @@ def decode_extra(layer, c, w, steps, warmup):
     counts = layer.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     wbytes = (touched + cd.S) * 3 * cd.H * cd.I * 2 + cd.E * cd.H * 2
-    iobytes = cd.T * cd.H * 2 * (2 + 2 * cd.k)     # x in, y out, x_perm and y_perm written and read
+    # rows of H bf16 per token: x for the router and the shared expert, y out, y_perm
+    # written and read, and x_perm written and read (copy) or x gathered (gather)
+    rows_per_token = 3 + 2 * cd.k + (cd.k if layer.gather else 2 * cd.k)
+    iobytes = cd.T * cd.H * 2 * rows_per_token
     return {"workload": cd.name, "T": cd.T, "ms_per_step": round(ms, 4), "tokens_per_s": round(cd.T / (ms * 1e-3), 1),
             "experts_touched": touched, "hbm_gbs": round((wbytes + iobytes) / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round((wbytes + iobytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes": wbytes + iobytes, "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+
+
+BWD_STAGES = ["combine_bwd", "expert_ffn_bwd", "route_bwd", "dispatch_bwd"]
+
+
+def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
+    """One training step of the layer at the prefill shape: the forward pass (with the
+    row copy, whose x_perm the backward reads) and the backward pass (gradients of
+    every weight, the input and the balance loss).  Per-call times from HIP events."""
+    import numpy as np
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    from biased_top_routing_amd.runner import MoeLayerGPU
+    from workloads.inputs import make_x
+
+    layer = MoeLayerGPU(c, w, gather=False)
+    x = to_dev(make_x(c, 0))
+    g = torch.Generator(device="cuda").manual_seed(5)
+    dy = torch.randn((c.T, c.H), device="cuda", generator=g).to(torch.bfloat16)
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    layer.alloc_backward()
+    cfg = layer.cfg
+
+    def bwd_calls():
+        return [lambda: L.moe_combine_backward(cfg, dy, layer.y_perm, layer.inv, layer.topk_w, layer.dy_perm,
+                                               layer.d_topk_w),
+                lambda: L.moe_expert_ffn_backward(cfg, layer.x_perm, x, layer.offsets, layer.weights, layer.dy_perm,
+                                                  dy, layer.dx_perm, layer.dx_shared, layer.grads, layer.ws_ffn_bwd),
+                lambda: L.moe_route_backward(cfg, x, layer.w_router, layer.scores, layer.topk_idx, layer.d_topk_w,
+                                             alpha, seq_len, layer.dx_router, layer.g_w_router, layer.loss_bal,
+                                             layer.ws_route_bwd),
+                lambda: L.moe_dispatch_backward(cfg, layer.dx_perm, layer.dx_shared, layer.dx_router, layer.inv,
+                                                layer.dx)]
+
+    calls = bwd_calls()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        layer.forward(x, bias, gamma=c.gamma)
+        for j, f in enumerate(calls):
+            if ev is not None:
+                ev[j + 1].record()
+            f()
+        if ev is not None:
+            ev[len(calls) + 1].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    fwd = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
+    st = {n: float(np.mean([ev[j + 1].elapsed_time(ev[j + 2]) for ev in events])) for j, n in enumerate(BWD_STAGES)}
+    rows = c.T * (c.k + c.S)
+    ffn_bwd_flops = 16 * c.H * c.I * rows            # recomputed gate/up 4HI, dh 2HI, dx 4HI, dW_gu 4HI, dW_d 2HI
+    router_bwd_flops = 4 * c.T * c.E * c.H
+    fwd_flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
+    ffn_tf = ffn_bwd_flops / (st["expert_ffn_bwd"] * 1e-3) / 1e12
+    out = {"workload": "v3_prefill_train_bf16", "T": c.T, "alpha": alpha, "seq_len": seq_len,
+           "ms_per_step": round(wall, 4), "tokens_per_s": round(c.T / (wall * 1e-3), 1),
+           "forward_ms": round(fwd, 4), "backward_ms": round(sum(st.values()), 4),
+           "backward_stages_ms": {k: round(v, 4) for k, v in st.items()},
+           "expert_ffn_bwd_tflops": round(ffn_tf, 2), "expert_ffn_bwd_frac_of_peak": round(ffn_tf / PEAK_BF16_TFLOPS, 4),
+           "step_tflops": round((fwd_flops + ffn_bwd_flops + router_bwd_flops) / (wall * 1e-3) / 1e12, 2),
+           "loss_bal": float(layer.loss_bal.item())}
+    del layer, x, dy
+    torch.cuda.empty_cache()
+    return out
 
 
 def balance_trajectory(layer, c, w, steps):
@@ -338,6 +417,9 @@ def main():
     w = make_weights(c)
     xh = make_x(c, 0)
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
+    if args.train_only:
+        print(json.dumps(train_extra(c, w, args.steps, args.warmup)), flush=True)
+        return
     gather = args.dispatch == "gather"
     layer = MoeLayerGPU(c, w, gather=gather)
     x = to_dev(xh)
@@ -413,6 +495,8 @@ def main():
         extras["route_sweep"] = route_sweep(c, w)
         del layer, x
         torch.cuda.empty_cache()
+        log("extra: one training step (forward + backward) at the prefill shape")
+        extras["v3_prefill_train_bf16"] = train_extra(c, w, max(args.steps // 2, 5), 2)
         cf = CONFIGS["v3_fp8"]
         log("extra: the FP8 layer (T=32768, Zipf-skewed routing)")
         wf = make_weights(cf)

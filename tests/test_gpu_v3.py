@@ -17,7 +17,8 @@ from biased_top_routing_amd import _lib as L
 from biased_top_routing_amd.runner import MoeLayerGPU, to_device
 from gpu_util import dev_f32, host, rel_inf, say
 from workloads import V3_PREFILL
-from workloads.inputs import make_weights, make_x, rng
+from oracle.layer import decode_act
+from workloads.inputs import f32_to_bf16_bits, make_weights, make_x, rng
 
 pytestmark = pytest.mark.gpu
 
@@ -136,3 +137,75 @@ def test_v3_prefill_gather_bit_exact(v3):
     torch.cuda.synchronize()
     assert torch.equal(y_perm.view(torch.int16), layer.y_perm.view(torch.int16))
     assert torch.equal(y_shared.view(torch.int16), layer.y_shared.view(torch.int16))
+
+
+def test_v3_prefill_backward_full_size(v3):
+    """The layer backward at the full V3-like size (the training step's shape), on
+    samples the fp64 oracle can afford: two whole experts' weight gradients, the
+    complete input gradient of sampled tokens (8 routed experts, the shared one,
+    the router and the balance term), d_topk_w of those tokens, dW_router (fp64
+    from the GPU's own d_topk_w) and the balance loss."""
+    from oracle.backward import gate_backward, seq_balance_loss, swiglu_backward
+    w, layer = v3
+    c = V3_PREFILL
+    alpha, seq_len = 1e-3, 4096
+    xh, _, _, _ = _run(c, w, layer, c.T, 0)   # forward (with the bias update: the routing is what counts)
+    x = to_device(xh)
+    dyh = f32_to_bf16_bits(rng(31, c.T).normal(size=(c.T, c.H)).astype(np.float32))
+    say("v3: backward")
+    layer.backward(x, to_device(dyh), alpha, seq_len)
+    torch.cuda.synchronize()
+    idx = host(layer.topk_idx).astype(np.int64)
+    dyf = decode_act(dyh).astype(np.float64)
+    say("v3: oracle affinities and balance term")
+    x64 = decode_act(xh).astype(np.float64)
+    wr = decode_act(w.w_router).astype(np.float64)
+    logits = x64 @ wr.T + (0.0 if w.logit_offset is None else np.asarray(w.logit_offset, np.float64))
+    s = 1.0 / (1.0 + np.exp(-logits))
+    loss, ds_bal = seq_balance_loss(s, idx, c.k, seq_len, alpha)
+    assert abs(float(host(layer.loss_bal)[0]) - loss) <= 1e-4 * loss
+    s_sel = np.take_along_axis(s, idx, axis=1)
+    gates = c.route_scale * s_sel / s_sel.sum(axis=1, keepdims=True)
+    # dW_router from the GPU's d_topk_w
+    dw_gpu = host(layer.d_topk_w).astype(np.float64)
+    ds = ds_bal.copy()
+    np.put_along_axis(ds, idx, np.take_along_axis(ds, idx, axis=1) + gate_backward(s_sel, dw_gpu, c.route_scale),
+                      axis=1)
+    dlogit = ds * s * (1.0 - s)
+    err = rel_inf(host(layer.g_w_router), dlogit.T @ x64)
+    say(f"  dW_router err {err:.2e}")
+    assert err < 2e-2
+    # sampled tokens: everything from scratch
+    rows = np.sort(rng(41, 6).choice(c.T, 6, replace=False))
+    wsgu = decode_act(w.ws_gate_up[0]).astype(np.float64)
+    wsd = decode_act(w.ws_down[0]).astype(np.float64)
+    dx_ref = np.zeros((len(rows), c.H))
+    dw_ref = np.zeros((len(rows), c.k))
+    for n, t in enumerate(rows):
+        xt = x64[t:t + 1]
+        for j in range(c.k):
+            e = idx[t, j]
+            wgu, wd = decode_act(w.w_gate_up[e]).astype(np.float64), decode_act(w.w_down[e]).astype(np.float64)
+            dw_ref[n, j] = float((dyf[t] * oracle.swiglu(xt, wgu, wd)[0]).sum())
+            dx_ref[n] += swiglu_backward(xt, wgu, wd, gates[t, j] * dyf[t:t + 1])[0][0]
+        dx_ref[n] += swiglu_backward(xt, wsgu, wsd, dyf[t:t + 1])[0][0]
+    ds_rows = ds_bal[rows].copy()
+    np.put_along_axis(ds_rows, idx[rows], np.take_along_axis(ds_rows, idx[rows], axis=1) +
+                      gate_backward(s_sel[rows], dw_ref, c.route_scale), axis=1)
+    dx_ref += (ds_rows * s[rows] * (1.0 - s[rows])) @ wr
+    e_dw = rel_inf(dw_gpu[rows], dw_ref)
+    e_dx = rel_inf(host(layer.dx)[rows], dx_ref)
+    say(f"  sampled d_topk_w err {e_dw:.2e}, dx err {e_dx:.2e}")
+    assert e_dw < 2e-2 and e_dx < 2e-2
+    # two whole experts' weight gradients (the two smallest non-empty segments)
+    counts = np.bincount(idx.reshape(-1), minlength=c.E)
+    for e in np.argsort(np.where(counts > 0, counts, 1 << 30), kind="stable")[:2]:
+        t_of, j_of = np.nonzero(idx == e)
+        say(f"  expert {e}: {len(t_of)} rows")
+        _, dwgu, dwd, _ = swiglu_backward(x64[t_of], decode_act(w.w_gate_up[e]).astype(np.float64),
+                                          decode_act(w.w_down[e]).astype(np.float64),
+                                          gates[t_of, j_of][:, None] * dyf[t_of])
+        e1 = rel_inf(host(layer.g_w_gate_up[e]), dwgu)
+        e2 = rel_inf(host(layer.g_w_down[e]), dwd)
+        say(f"    dW_gate_up err {e1:.2e}, dW_down err {e2:.2e}")
+        assert e1 < 2e-2 and e2 < 2e-2
