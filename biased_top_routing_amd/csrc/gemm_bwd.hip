@@ -298,43 +298,67 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bwd_kernel(BwdParams p) 
   for (int kt = 0; kt < nk; ++kt) {
     wait_slices<PER>(min(nk - 1, kt + STAGES - 2) - kt);
     asm volatile("s_barrier" ::: "memory");
+    const bf16_t* base = lds + cur * STAGE;
+    const bf16_t* bbase = base + BM * BK;
+    constexpr int KK = BK / 16;
+    // Every transposing read of this slice is issued before the next slice's
+    // direct-to-LDS loads: issued after them, the compiler makes the first one
+    // wait for those loads (vmcnt(0)), which serialises loads and MFMAs.
+    bf16x8_t fbs[KK][NI];
+    bf16x8_t fas[A_MC ? KK : 1][MI];
+    if (has_rows) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) fbs[kk][ni] = mc_frag<BN>(bbase, kk, wn * NI * 32 + ni * 32, lane);
+        if constexpr (A_MC) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) fas[kk][mi] = mc_frag<BM>(base, kk, wm * MI * 32 + mi * 32, lane);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (kt + STAGES - 1 < nk) {
       const int st = cur == 0 ? STAGES - 1 : cur - 1;
       MOE_ISSUE_BWD(st, (kt + STAGES - 1) * BK);
     }
-    const bf16_t* base = lds + cur * STAGE;
-    const bf16_t* bbase = base + BM * BK;
-    constexpr int KK = BK / 16;
     if (has_rows) {
-      bf16x8_t fa[2][MI], fb[2][NI];
-#define MOE_READ_FRAGS(kk_, buf_)                                                                       \
-  {                                                                                                     \
-    _Pragma("unroll") for (int mi = 0; mi < MI; ++mi) {                                                 \
-      if constexpr (A_MC) fa[buf_][mi] = mc_frag<BM>(base, (kk_), wm * MI * 32 + mi * 32, lane);          \
-      else                                                                                              \
-        fa[buf_][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK +                          \
-                                                          (swz<8>(a_rd[mi], 2 * (kk_) + kh) << 3));      \
-    }                                                                                                   \
-    _Pragma("unroll") for (int ni = 0; ni < NI; ++ni)                                                   \
-        fb[buf_][ni] = mc_frag<BN>(bbase, (kk_), wn * NI * 32 + ni * 32, lane);                          \
-  }
-      MOE_READ_FRAGS(0, 0);
+      if constexpr (A_MC) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int cb = kk & 1;
-        if (kk + 1 < KK) MOE_READ_FRAGS(kk + 1, cb ^ 1);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fas[kk][mi], fbs[kk][ni], acc[mi][ni], 0, 0, 0);
+        }
+      } else {
+        // K-contiguous A: ds_read_b128 fragments, double-buffered across the k-steps
+        bf16x8_t fa[2][MI];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
+          fa[0][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + (swz<8>(a_rd[mi], kh) << 3));
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fb[cb][ni], acc[mi][ni], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < KK; ++kk) {
+          const int cb = kk & 1;
+          if (kk + 1 < KK) {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+              fa[cb ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK +
+                                                                  (swz<8>(a_rd[mi], 2 * (kk + 1) + kh) << 3));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][mi], fbs[kk][ni], acc[mi][ni], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     cur = cur == STAGES - 1 ? 0 : cur + 1;
   }
-#undef MOE_READ_FRAGS
 #undef MOE_ISSUE_BWD
 
   // ------------------------------------------------------------ epilogue
