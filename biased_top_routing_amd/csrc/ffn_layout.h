@@ -33,10 +33,13 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 #ifndef MOE_DN_TILE
 #define MOE_DN_TILE 4, 4, 2, 2, 64, 2, 1
 #endif
-// Router GEMM tile (tokens x experts): 64 x 256, 8 wavefronts, 3-slice ring
+// Router GEMM tiles (tokens x experts): 64, 128 or 256 tokens x 256 experts,
+// 8 wavefronts; the launcher picks the tallest that still fills the GPU
 #ifndef MOE_RT_TILE
 #define MOE_RT_TILE 2, 4, 1, 2, 64, 3, 1
 #endif
+#define MOE_RT128_TILE 2, 4, 2, 2, 64, 3, 1
+#define MOE_RT256_TILE 2, 4, 4, 2, 64, 2, 1
 template <int WM_, int WN_, int MI_, int NI_, int BK_, int STAGES_, int OCC_>
 struct TileCfg {
   static constexpr int WM = WM_, WN = WN_, MI = MI_, NI = NI_, BK = BK_, STAGES = STAGES_, OCC = OCC_;

@@ -213,3 +213,27 @@ def test_layer_determinism_and_routing_invariants():
     assert np.abs(w.astype(np.float64).sum(1) - c.route_scale).max() <= c.k * ulp
     sel = np.take_along_axis(s.astype(np.float64), idx.astype(np.int64), 1)
     np.testing.assert_allclose(w, c.route_scale * sel / sel.sum(1, keepdims=True), rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("T", [16384, 32768, 65613])
+def test_router_gemm_tile_heights(T):
+    """The router GEMM's tile height follows the batch (64, 128, 256 tokens here; the
+    last with a ragged final tile): affinities against the fp64 oracle, routing
+    teacher-forced bit for bit."""
+    from biased_top_routing_amd import _lib as L
+    c = MID.with_(T=T, H=256, E=64, I=128, S=1)
+    w = make_weights(c)
+    xh = make_x(c)
+    say(f"router T={T}")
+    cfg = L.cfg_from(c)
+    s = torch.empty((T, c.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((T, c.k), dtype=torch.float32, device="cuda")
+    L.moe_route(cfg, to_device(xh), to_device(w.w_router), to_device(w.logit_offset), dev_f32(w.bias0), s, 0, idx, wt)
+    torch.cuda.synchronize()
+    s_gpu = host(s)
+    s_ora = oracle.affinity(oracle.decode_act(xh).astype(np.float64), oracle.decode_act(w.w_router).astype(np.float64),
+                            w.logit_offset)
+    assert np.abs(s_gpu - s_ora).max() < 1e-5
+    idx_o, _ = oracle.route(s_gpu, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale)
+    assert (host(idx) == idx_o).all()
