@@ -273,36 +273,39 @@ __global__ __launch_bounds__(256) void route_topk16_kernel(
       rank += (o > gs) || (o == gs && h < grp);
     }
     const bool chosen = rank < M;
-    // ---- k rounds of the 16-lane max
-    uint64_t key[EPL];
+    // ---- k rounds of the 16-lane max.  Keys are the 32-bit order keys of q
+    // (0 = not selectable: a non-chosen group, a cleared winner, a token past
+    // T).  A round takes the largest key (per-lane max, then a 16-lane DPP
+    // max), then among the lanes holding it the lowest expert index (DPP min),
+    // so ties go to the lower index; the winner clears its entry.  The gate
+    // values are read back from the score row at the end.
+    uint32_t key[EPL];
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      const uint32_t e = (uint32_t)(sl * EPL + j);
-      key[j] = (valid && chosen) ? (((uint64_t)float_order_key(q[j]) << 32) | (uint64_t)(0xFFFFFFFFu - e)) : 0ull;
-    }
+    for (int j = 0; j < EPL; ++j) key[j] = (valid && chosen) ? float_order_key(q[j]) : 0u;
     int my_e = 0;
-    float my_s = 0.f;
     for (int r = 0; r < k; ++r) {
-      uint64_t best = key[0];
-      float bs = s[0];
+      uint32_t m = key[0];
 #pragma unroll
-      for (int j = 1; j < EPL; ++j) {
-        const bool gt = key[j] > best;
-        best = gt ? key[j] : best;
-        bs = gt ? s[j] : bs;
-      }
-      max_step<kDppXor1>(best, bs);
-      max_step<kDppXor2>(best, bs);
-      max_step<kDppHalfMirror>(best, bs);
-      max_step<kDppMirror>(best, bs);
-      if (sl == r) {
-        my_e = (int)(0xFFFFFFFFu - (uint32_t)best);
-        my_s = bs;
-      }
+      for (int j = 1; j < EPL; ++j) m = max(m, key[j]);
+      m = max(m, dpp_u32<kDppXor1>(m));
+      m = max(m, dpp_u32<kDppXor2>(m));
+      m = max(m, dpp_u32<kDppHalfMirror>(m));
+      m = max(m, dpp_u32<kDppMirror>(m));
+      int jl = EPL;                                   // lowest local position holding the max
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) key[j] = key[j] == best ? 0ull : key[j];
+      for (int j = EPL - 1; j >= 0; --j) jl = key[j] == m ? j : jl;
+      uint32_t we = jl < EPL ? (uint32_t)(sl * EPL + jl) : 0xFFFFFFFFu;
+      we = min(we, dpp_u32<kDppXor1>(we));
+      we = min(we, dpp_u32<kDppXor2>(we));
+      we = min(we, dpp_u32<kDppHalfMirror>(we));
+      we = min(we, dpp_u32<kDppMirror>(we));
+      const int jw = (int)we - sl * EPL;              // in [0, EPL) on the winning lane only
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) key[j] = j == jw ? 0u : key[j];
+      if (sl == r) my_e = (int)we;
     }
-    float tot = sl < k ? my_s : 0.f;
+    const float my_s = (valid && sl < k) ? row[my_e - sl * EPL] : 0.f;
+    float tot = my_s;
     tot += dpp_f32<kDppXor1>(tot);
     tot += dpp_f32<kDppXor2>(tot);
     tot += dpp_f32<kDppHalfMirror>(tot);
