@@ -44,16 +44,18 @@ __device__ __forceinline__ uint4 f32_to_bf16x8(const float* f) {
 
 constexpr int kMaxTopK = 32;   // validate_cfg bounds k
 
-// One workgroup per token: for each slot j, d_topk_w[t,j] = <dy_t, y_perm[inv_tj]>
-// (fp32 over 16-byte chunks, per-wave shuffle sums, then the 4 waves in order)
-// and dy_perm[inv_tj] = topk_w[t,j] * dy_t.
-__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
+// One workgroup per token, one lane per 16-byte chunk of the row (up to 1024
+// lanes): for each slot j, d_topk_w[t,j] = <dy_t, y_perm[inv_tj]> (fp32,
+// per-wave shuffle sums, then the waves in order) and dy_perm[inv_tj] =
+// topk_w[t,j] * dy_t.
+constexpr int kMaxWaves = 16;
+__global__ __launch_bounds__(1024) void combine_bwd_kernel(const uint4* __restrict__ dy,
                                                           const uint4* __restrict__ y_perm,
                                                           const int32_t* __restrict__ inv,
                                                           const float* __restrict__ topk_w, int k,
                                                           int64_t nchunk, uint4* __restrict__ dy_perm,
                                                           float* __restrict__ d_w) {
-  __shared__ float red[4][kMaxTopK];
+  __shared__ float red[kMaxWaves][kMaxTopK];
   const int64_t t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int j = 0; j < k; ++j) {
@@ -76,13 +78,16 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
   }
   __syncthreads();
   if ((int)threadIdx.x < k) {
-    const int j = threadIdx.x;
-    d_w[t * k + j] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+    const int j = threadIdx.x, nw = (int)(blockDim.x / kWave);
+    float v = red[0][j];
+    for (int w = 1; w < nw; ++w) v += red[w][j];
+    d_w[t * k + j] = v;
   }
 }
 
-// dx_t = sum_j dx_perm[inv_tj] + dx_shared_t + dx_router_t (fp32, in that order), bf16 out.
-__global__ __launch_bounds__(256) void dispatch_bwd_kernel(const uint4* __restrict__ dx_perm,
+// dx_t = sum_j dx_perm[inv_tj] + dx_shared_t + dx_router_t (fp32, in that order), bf16 out;
+// one lane per 16-byte chunk of the row.
+__global__ __launch_bounds__(1024) void dispatch_bwd_kernel(const uint4* __restrict__ dx_perm,
                                                            const uint4* __restrict__ dx_shared,
                                                            const float4* __restrict__ dx_router,
                                                            const int32_t* __restrict__ inv, int k,
@@ -230,6 +235,11 @@ __global__ __launch_bounds__(256) void route_grad_kernel(const float* __restrict
 
 bool bwd_dtypes_ok(const moe_cfg* c) { return c->act == MOE_BF16 && c->wgt == MOE_BF16; }
 
+// one lane per 16-byte chunk of a row, whole wavefronts, at most 1024 lanes
+dim3 row_block(int64_t nchunk) {
+  return dim3((unsigned)std::min<int64_t>(align_up((size_t)nchunk, kWave), kMaxWaves * kWave));
+}
+
 }  // namespace
 
 }  // namespace moe
@@ -245,7 +255,7 @@ extern "C" moe_status moe_combine_backward(const moe_cfg* cfg, const void* dy, c
   if (!dy || !y_perm || !inv || !topk_w || !dy_perm || !d_topk_w) return MOE_ERR_NULL;
   if (cfg->T == 0) return MOE_OK;
   const int64_t nchunk = (int64_t)cfg->H * 2 / 16;
-  hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)cfg->T), dim3(256), 0, as_stream(stream), (const uint4*)dy,
+  hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)cfg->T), row_block(nchunk), 0, as_stream(stream), (const uint4*)dy,
                      (const uint4*)y_perm, inv, topk_w, cfg->k, nchunk, (uint4*)dy_perm, d_topk_w);
   return launch_status();
 }
@@ -319,7 +329,7 @@ extern "C" moe_status moe_dispatch_backward(const moe_cfg* cfg, const void* dx_p
   if (!dx_perm || !inv || !dx || (cfg->S > 0 && !dx_shared)) return MOE_ERR_NULL;
   if (cfg->T == 0) return MOE_OK;
   const int64_t nchunk = (int64_t)cfg->H * 2 / 16;
-  hipLaunchKernelGGL(dispatch_bwd_kernel, dim3((unsigned)cfg->T), dim3(256), 0, as_stream(stream),
+  hipLaunchKernelGGL(dispatch_bwd_kernel, dim3((unsigned)cfg->T), row_block(nchunk), 0, as_stream(stream),
                      (const uint4*)dx_perm, cfg->S > 0 ? (const uint4*)dx_shared : nullptr,
                      (const float4*)dx_router, inv, cfg->k, nchunk, (uint4*)dx);
   return launch_status();

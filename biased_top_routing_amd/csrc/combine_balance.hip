@@ -6,12 +6,16 @@
 // update follows the reading notes (Method §1 "Auxiliary-loss-free 负载均衡")
 // and the qwbw.cn essay's load-balancing section: after each step an
 // overloaded expert's bias falls by gamma and an underloaded one's rises.
+#include <algorithm>
+
 #include "common.h"
 
 namespace moe {
 
-// One workgroup per token (its row's 16-byte chunks spread over 256 lanes;
-// 8 bf16 or 4 fp32 values per chunk).
+// One workgroup per token with one lane per 16-byte chunk of the row (8 bf16 or
+// 4 fp32 values; up to 1024 lanes, whole wavefronts): every routed row of a
+// token is in flight at once (measured at 7168 bf16 columns: 896 lanes 9%
+// faster than 256 lanes looping over 3.5 chunks each).
 // y = y_shared + sum_j w_j * y_perm[inv_j], fp32 accumulation, j ascending.
 // The k routed rows of a chunk are loaded in batches of 8 before they are
 // accumulated, so that a lane keeps up to 9 loads in flight.  Each output row
@@ -53,7 +57,7 @@ __device__ __forceinline__ void accum_chunk(float* acc, uint4 r, float g) {
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y_perm,
+__global__ __launch_bounds__(1024) void combine_kernel(const uint4* __restrict__ y_perm,
                                                       const uint4* __restrict__ y_shared,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ topk_w, int T,
@@ -125,12 +129,13 @@ extern "C" moe_status moe_combine(const moe_cfg* cfg, const void* y_perm, const 
   if (cfg->T == 0) return MOE_OK;
   const int64_t nchunk = (int64_t)cfg->H * act_bytes(cfg) / 16;
   const dim3 grid((unsigned)cfg->T);
+  const dim3 block((unsigned)std::min<int64_t>(align_up((size_t)nchunk, kWave), 1024));
   const uint4* ysh = cfg->S > 0 ? (const uint4*)y_shared : nullptr;
   if (cfg->act == MOE_F32)
-    hipLaunchKernelGGL((combine_kernel<false>), grid, dim3(256), 0, as_stream(stream), (const uint4*)y_perm,
+    hipLaunchKernelGGL((combine_kernel<false>), grid, block, 0, as_stream(stream), (const uint4*)y_perm,
                        ysh, inv, topk_w, cfg->T, cfg->k, nchunk, (uint4*)y);
   else
-    hipLaunchKernelGGL((combine_kernel<true>), grid, dim3(256), 0, as_stream(stream), (const uint4*)y_perm,
+    hipLaunchKernelGGL((combine_kernel<true>), grid, block, 0, as_stream(stream), (const uint4*)y_perm,
                        ysh, inv, topk_w, cfg->T, cfg->k, nchunk, (uint4*)y);
   return launch_status();
 }

@@ -86,15 +86,17 @@ __device__ __forceinline__ bf16x8_t mc_frag(const bf16_t* tile, int kk, int mb, 
 }
 #endif
 
-template <int KIND, int WM, int WN, int MI, int NI, int STAGES>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bwd_kernel(BwdParams p) {
+template <int KIND, int WM, int WN, int MI, int NI, int STAGES, int BK, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p) {
   constexpr bool KSEG = kseg_kind(KIND);
   constexpr bool A_MC = KSEG;          // A is M-contiguous exactly for the weight gradients
-  constexpr int NW = WM * WN, NT = 64 * NW, BK = 64;
+  constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int BM = WM * MI * 32, BN = WN * NI * 32;
-  constexpr int A_CH = BM * 8 / NT, B_CH = BN * 8 / NT, PER = A_CH + B_CH;
+  constexpr int CPK = BK / 8;          // 16-byte chunks per K-contiguous row of a slice
+  constexpr int A_CH = BM * CPK / NT, B_CH = BN * CPK / NT, PER = A_CH + B_CH;
   constexpr int STAGE = (BM + BN) * BK;
-  static_assert(BM * 8 % NT == 0 && BN * 8 % NT == 0, "whole loads per thread");
+  static_assert(BK == 32 || BK == 64, "K slices of 32 or 64");
+  static_assert(BM * CPK % NT == 0 && BN * CPK % NT == 0, "whole loads per thread");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "M-contiguous slices of at least 16 chunks per row");
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * STAGE];
@@ -243,8 +245,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bwd_kernel(BwdParams p) 
       const int r = q / CPR, pc = q % CPR;
       a_off[i] = (r * lda + m0 + ((pc ^ mc_key(r)) << 3)) * 2;
     } else {
-      const int r = q >> 3, pc = q & 7;
-      a_off[i] = ((r < mvalid ? r : mvalid + 1) * lda + (swz<8>(r, pc) << 3)) * 2;
+      const int r = q / CPK, pc = q % CPK;
+      a_off[i] = ((r < mvalid ? r : mvalid + 1) * lda + (swz<CPK>(r, pc) << 3)) * 2;
     }
   }
 #pragma unroll
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bwd_kernel(BwdParams p) 
         bf16x8_t fa[2][MI];
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
-          fa[0][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + (swz<8>(a_rd[mi], kh) << 3));
+          fa[0][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK + (swz<CPK>(a_rd[mi], kh) << 3));
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const int cb = kk & 1;
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bwd_kernel(BwdParams p) 
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
               fa[cb ^ 1][mi] = *reinterpret_cast<const bf16x8_t*>(base + a_rd[mi] * BK +
-                                                                  (swz<8>(a_rd[mi], 2 * (kk + 1) + kh) << 3));
+                                                                  (swz<CPK>(a_rd[mi], 2 * (kk + 1) + kh) << 3));
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -418,9 +420,21 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
   out[i] = s;
 }
 
-#define MOE_BWD_TILE 2, 4, 4, 2, 2
+// dh, dx, router: 256 x 256 tiles, 8 wavefronts, 64-deep slices in a 2-slice ring, one workgroup per CU.
+#define MOE_BWD_TILE 2, 4, 4, 2, 2, 64, 1
 constexpr int kBwdThreads = 64 * 2 * 4;
 static_assert(2 * 4 * 32 == kBwdBM && 4 * 2 * 32 == kBwdBN, "backward tile shape");
+// Expert weight gradients: the same 256 x 256 tile (measured: 256 x 128 tiles with 32-deep slices and two
+// workgroups per CU, one computing while the other drains its fp32 stores, are 5-10% slower).
+#ifndef MOE_BWD_WG_TILE
+#define MOE_BWD_WG_TILE 2, 4, 4, 2, 2, 64, 1
+#endif
+template <int WM_, int WN_, int MI_, int NI_, int STAGES_, int BK_, int OCC_>
+struct BwdTile {
+  static constexpr int WM = WM_, WN = WN_, MI = MI_, NI = NI_, STAGES = STAGES_, BK = BK_, OCC = OCC_;
+  static constexpr int BM = WM * MI * 32, BN = WN * NI * 32, THREADS = 64 * WM * WN;
+};
+using WgTile = BwdTile<MOE_BWD_WG_TILE>;
 
 static inline unsigned grid_of(int64_t n) { return (unsigned)align_up((size_t)(n > 0 ? n : 0), 8); }
 
@@ -471,7 +485,9 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   hipLaunchKernelGGL((gemm_bwd_kernel<kDx, MOE_BWD_TILE>), dim3(grid_of(L.max_dx)), dim3(kBwdThreads), 0, st, p);
   if ((s = launch_status()) != MOE_OK) return s;
   // weight gradients
-  auto tiles_of = [](int64_t m, int64_t n) { return ((m + kBwdBM - 1) / kBwdBM) * ((n + kBwdBN - 1) / kBwdBN); };
+  auto tiles_of = [](int64_t m, int64_t n) {
+    return ((m + WgTile::BM - 1) / WgTile::BM) * ((n + WgTile::BN - 1) / WgTile::BN);
+  };
   const int64_t SI = (int64_t)c->S * c->I;
   p.a_routed = dgu; p.a_shared = dgus;
   p.b_routed = x_perm; p.b_shared = x;
@@ -479,7 +495,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   {
     const int64_t n_sh = c->S > 0 ? tiles_of(2 * SI, c->H) : 0;
     const int64_t n = grid_of(n_sh) + grid_of(c->E * tiles_of(2 * c->I, c->H));
-    hipLaunchKernelGGL((gemm_bwd_kernel<kDwGu, MOE_BWD_TILE>), dim3((unsigned)n), dim3(kBwdThreads), 0, st, p);
+    hipLaunchKernelGGL((gemm_bwd_kernel<kDwGu, MOE_BWD_WG_TILE>), dim3((unsigned)n), dim3(WgTile::THREADS), 0, st, p);
     if ((s = launch_status()) != MOE_OK) return s;
   }
   p.a_routed = dy_perm; p.a_shared = dy;
@@ -488,7 +504,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   {
     const int64_t n_sh = c->S > 0 ? tiles_of(c->H, SI) : 0;
     const int64_t n = grid_of(n_sh) + grid_of(c->E * tiles_of(c->H, c->I));
-    hipLaunchKernelGGL((gemm_bwd_kernel<kDwD, MOE_BWD_TILE>), dim3((unsigned)n), dim3(kBwdThreads), 0, st, p);
+    hipLaunchKernelGGL((gemm_bwd_kernel<kDwD, MOE_BWD_WG_TILE>), dim3((unsigned)n), dim3(WgTile::THREADS), 0, st, p);
     if ((s = launch_status()) != MOE_OK) return s;
   }
   return MOE_OK;
