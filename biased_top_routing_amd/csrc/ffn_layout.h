@@ -39,6 +39,7 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 #define MOE_RT_TILE 2, 4, 1, 2, 64, 3, 1
 #endif
 #define MOE_RT128_TILE 2, 4, 2, 2, 64, 3, 1
+#define MOE_RT128N_TILE 2, 4, 2, 1, 64, 3, 1
 #define MOE_RT256_TILE 2, 4, 4, 2, 64, 2, 1
 template <int WM_, int WN_, int MI_, int NI_, int BK_, int STAGES_, int OCC_>
 struct TileCfg {

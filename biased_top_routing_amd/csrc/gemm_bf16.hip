@@ -342,9 +342,11 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   p.offset = offset;
   p.out_routed = scores;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-  // Every token tile re-reads the whole router weight (E x H) from L2, so the
-  // tile is as tall as the batch allows while the grid still covers every CU:
-  // 64 tokens at T = 16384 (256 tiles), up to 256 tokens for large batches.
+  // Every token tile re-reads its columns of the router weight from L2, so the
+  // tile is as large as the batch allows while the grid still covers every CU:
+  // 256 x 256 and 128 x 256 for large batches, 128 x 128 at T = 16384 (two
+  // column tiles of 128 experts: 3.5 instead of 4.6 MB of operand loads per tile
+  // against 64 x 256, measured 14% faster), else 64 x 256.
   static int n_cu = 0;
   if (n_cu == 0) {
     int dev = 0, n = 0;
@@ -353,16 +355,22 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
       n = 256;
     n_cu = n;
   }
-  const int64_t ncol = (c->E + 255) / 256;
-  auto tiles = [&](int bm) { return ((int64_t)c->T + bm - 1) / bm * ncol; };
+  auto tiles = [&](auto cfg) {
+    using RT = decltype(cfg);
+    return ((int64_t)c->T + RT::BM - 1) / RT::BM * (((int64_t)c->E + RT::BN - 1) / RT::BN);
+  };
   auto launch = [&](auto cfg) {
     using RT = decltype(cfg);
     const dim3 grid((unsigned)((c->T + RT::BM - 1) / RT::BM), (unsigned)((c->E + RT::BN - 1) / RT::BN));
     hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, RT::WM, RT::WN, RT::MI, RT::NI, RT::BK, RT::STAGES, RT::OCC>), grid,
                        dim3(64 * RT::WM * RT::WN), 0, st, p);
   };
-  if (tiles(256) >= n_cu) launch(TileCfg<MOE_RT256_TILE>{});
-  else if (tiles(128) >= n_cu) launch(TileCfg<MOE_RT128_TILE>{});
+  using RT256 = TileCfg<MOE_RT256_TILE>;
+  using RT128 = TileCfg<MOE_RT128_TILE>;
+  using RT128N = TileCfg<MOE_RT128N_TILE>;
+  if (tiles(RT256{}) >= n_cu) launch(RT256{});
+  else if (tiles(RT128{}) >= n_cu) launch(RT128{});
+  else if (tiles(RT128N{}) >= n_cu) launch(RT128N{});
   else launch(TileCfg<MOE_RT_TILE>{});
   return launch_status();
 }
