@@ -49,6 +49,14 @@ struct TileCfg {
 using GateUpTile = TileCfg<MOE_GU_TILE>;
 using DownTile = TileCfg<MOE_DN_TILE>;
 constexpr int kBM1 = GateUpTile::BM;      // token rows of a gate/up tile
+// A segment's gate/up row tiles are kBM1Alt rows high instead of kBM1 when that
+// takes no more tiles: fewer padded MFMA rows (e.g. 512 rows: two tiles of 256
+// instead of 320 + 192), run by a kernel body with MOE_GU_MI_ALT row blocks per
+// wavefront.  0 turns this off.
+#ifndef MOE_GU_MI_ALT
+#define MOE_GU_MI_ALT 4
+#endif
+constexpr int kBM1Alt = GateUpTile::WM * MOE_GU_MI_ALT * 32;
 constexpr int kBM2 = DownTile::BM;        // token rows of a down tile
 constexpr int kBNH = GateUpTile::BN / 2;   // h columns of a gate/up tile (as many gate as up weight rows)
 constexpr int kBN2 = DownTile::BN;         // output columns of a down tile
@@ -95,6 +103,7 @@ struct TileDesc {
 struct FfnLayout {
   bool dec;                      // small-batch bf16 configuration
   int bm1, bm2;                  // token rows per tile: gate/up, down
+  int bm1_alt;                   // gate/up rows per tile where that takes no more tiles (0: bm1 only)
   int64_t R1, Rs1, R2, Rs2;      // routed row-tile bounds, shared row tiles
   int64_t nt1, nt1s, nt2;        // column tiles: gate/up routed, gate/up shared, down
   int64_t max1, max2;            // tile-table capacities
@@ -106,6 +115,7 @@ struct FfnLayout {
     const bool f8 = c->wgt == MOE_FP8_E4M3;
     dec = small_batch(c);
     bm1 = f8 ? kFp8BM : dec ? kDecBM : kBM1;
+    bm1_alt = f8 || dec ? 0 : kBM1Alt;
     bm2 = f8 ? kFp8BM : dec ? kDecBM : kBM2;
     R1 = P / bm1 + c->E;
     Rs1 = c->S > 0 ? (c->T + bm1 - 1) / bm1 : 0;

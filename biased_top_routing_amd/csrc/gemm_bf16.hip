@@ -50,9 +50,10 @@ struct GemmParams {
 
 // Tile of (WM*MI*32) token rows x (WN*NI*32) weight rows; wave (wm, wn) owns
 // MI x NI MFMA 32x32 blocks.  K advances BK columns per slice through a ring of
-// STAGES LDS stages filled by direct-to-LDS loads.
-template <int MODE, int WM, int WN, int MI, int NI, int BK, int STAGES, int OCC>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams p) {
+// STAGES LDS stages filled by direct-to-LDS loads.  `lds` holds STAGES stages.
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+template <int MODE, int WM, int WN, int MI, int NI, int BK, int STAGES>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int seg, int row0, int rows, int nt) {
   constexpr int NW = WM * WN;             // wavefronts per workgroup
   constexpr int NT = 64 * NW;             // threads
   static_assert(NW == 4 || NW == 8 || NW == 16, "4, 8 or 16 wavefronts per workgroup");
@@ -64,32 +65,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   constexpr int PER = A_CH + B_CH;
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-  __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * STAGE];
-
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-
-  // ------------------------------------------------------------ which tile
-  int seg = 0, row0, rows, nt;
-  if constexpr (MODE == kRouter) {
-    row0 = blockIdx.x * BM;
-    rows = min(BM, p.T - row0);
-    nt = blockIdx.y;
-  } else {
-    const int n_real = __builtin_amdgcn_readfirstlane(*p.ntiles);
-    const int per = (n_real + 7) >> 3;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    if (j >= per) return;
-    const int L = xcd * per + j;
-    if (L >= n_real) return;
-    const TileDesc d = p.tiles[L];
-    // the descriptor is the same for the whole workgroup: keep it in SGPRs
-    seg = __builtin_amdgcn_readfirstlane(d.seg);
-    row0 = __builtin_amdgcn_readfirstlane(d.row0);
-    rows = __builtin_amdgcn_readfirstlane(d.rows);
-    nt = __builtin_amdgcn_readfirstlane(d.nt);
-  }
   const bool shared = (MODE != kRouter) && seg == p.E;
   // Routed gate/up rows gathered straight from x: row row0 + r of the
   // expert-sorted order is token perm[row0 + r] / k (dispatch's row copy
@@ -331,7 +308,66 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
       }
     }
   }
+}
 #endif
+
+// One workgroup per tile.  Grouped GEMMs (MI_ALT > 0): a tile whose valid rows
+// fit fewer MFMA rows with MI_ALT blocks per wavefront (e.g. 161..256 rows:
+// 256 with MI_ALT = 4 against 320 with MI = 5) runs the MI_ALT body; both
+// bodies share the LDS ring (sized for MI).
+template <int MODE, int WM, int WN, int MI, int NI, int BK, int STAGES, int OCC, int MI_ALT = 0>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams p) {
+  static_assert(MI_ALT >= 0 && MI_ALT < MI, "the alternative body has fewer row blocks");
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = WM * MI * 32;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * (BM + WN * NI * 32) * BK];
+  // ------------------------------------------------------------ which tile
+  int seg = 0, row0, rows, nt;
+  if constexpr (MODE == kRouter) {
+    row0 = blockIdx.x * BM;
+    rows = min(BM, p.T - row0);
+    nt = blockIdx.y;
+  } else {
+    // Each XCD takes an equal share of the shared-expert tiles first, then an
+    // equal share of the routed ones (routed tiles differ in height, shared
+    // ones are all full: cutting the table by count alone left the XCD that
+    // held the shared tiles last to finish).
+    const int n_real = __builtin_amdgcn_readfirstlane(p.ntiles[0]);
+    const int n_rt = __builtin_amdgcn_readfirstlane(p.ntiles[4]);
+    const int per_s = (n_real - n_rt + 7) >> 3, per_r = (n_rt + 7) >> 3;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    int L;
+    if (j < per_s) {
+      L = n_rt + xcd * per_s + j;
+      if (L >= n_real) return;
+    } else {
+      if (j - per_s >= per_r) return;
+      L = xcd * per_r + (j - per_s);
+      if (L >= n_rt) return;
+    }
+    const TileDesc d = p.tiles[L];
+    // the descriptor is the same for the whole workgroup: keep it in SGPRs
+    seg = __builtin_amdgcn_readfirstlane(d.seg);
+    row0 = __builtin_amdgcn_readfirstlane(d.row0);
+    rows = __builtin_amdgcn_readfirstlane(d.rows);
+    nt = __builtin_amdgcn_readfirstlane(d.nt);
+  }
+  if constexpr (MI_ALT > 0) {
+    // MFMA rows computed: whole wavefront row bands of MI*32 (or MI_ALT*32) rows
+    constexpr int HM = MI * 32, HA = MI_ALT * 32;
+    if (rows <= WM * HA && (rows + HA - 1) / HA * HA < (rows + HM - 1) / HM * HM) {
+      gemm_tile<MODE, WM, WN, MI_ALT, NI, BK, STAGES>(p, lds, seg, row0, rows, nt);
+      return;
+    }
+  }
+  gemm_tile<MODE, WM, WN, MI, NI, BK, STAGES>(p, lds, seg, row0, rows, nt);
+#endif
+}
+
+// Workgroups of a grouped launch over a table of at most max_tiles tiles: the
+// shared and routed shares of each XCD round up apart (two more per XCD).
+static int64_t grouped_grid(int64_t max_tiles) {
+  return max_tiles > 0 ? (int64_t)align_up((size_t)max_tiles, 8) + 16 : 0;
 }
 
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
@@ -394,13 +430,13 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.ntiles = hdr;
     p.perm = perm;
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
-    const int64_t grid = align_up((size_t)L.max1, 8);
+    const int64_t grid = grouped_grid(L.max1);
     if (grid > 0) {
       if (L.dec)
         hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_DEC_GU_TILE>), dim3((unsigned)grid),
                            dim3(64 * DecGateUpTile::WM * DecGateUpTile::WN), 0, st, p);
       else
-        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE, MOE_GU_MI_ALT>), dim3((unsigned)grid),
                            dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
@@ -413,7 +449,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t2);
     p.ntiles = hdr + 1;
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-    const int64_t grid = align_up((size_t)L.max2, 8);
+    const int64_t grid = grouped_grid(L.max2);
     if (grid > 0) {
       if (L.dec)
         hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DEC_DN_TILE>), dim3((unsigned)grid),
@@ -439,9 +475,9 @@ moe_status launch_gateup_recompute_bf16(const moe_cfg* c, const bf16_t* x_perm, 
   p.tiles = tiles;
   p.ntiles = ntiles;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
-  const int64_t grid = align_up((size_t)max_tiles, 8);
+  const int64_t grid = grouped_grid(max_tiles);
   if (grid > 0)
-    hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpGU, MOE_GU_TILE>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpGU, MOE_GU_TILE, MOE_GU_MI_ALT>), dim3((unsigned)grid),
                        dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
   return launch_status();
 }
