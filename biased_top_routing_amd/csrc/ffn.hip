@@ -26,13 +26,14 @@ namespace moe {
 // tiles in flight.  Every workgroup computes the prefix sums over segments in LDS
 // (at most 513 segments) and writes its own share of the entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
-                                                           int S, int T, int bm1, int bm1_alt, int bm2, int nt1,
-                                                           int nt1s,
+                                                           int S, int T, int bm1, int bm1_alt, int bm2,
+                                                           int bm2_alt, int nt1, int nt1s,
                                                            int nt2,
                                                            TileDesc* __restrict__ t1,
                                                            TileDesc* __restrict__ t2,
                                                            int32_t* __restrict__ hdr) {
-  __shared__ int32_t pre1[1024], pre2[1024], mt1_s[1024], mt2_s[1024], row0_s[1024], rows_s[1024], hb1_s[1024];
+  __shared__ int32_t pre1[1024], pre2[1024], mt1_s[1024], mt2_s[1024], row0_s[1024], rows_s[1024], hb1_s[1024],
+      hb2_s[1024];
   const int tid = threadIdx.x;
   const int nseg = E + (S > 0 ? 1 : 0);
   int c1 = 0, c2 = 0;
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     const int mt1 = (rows + bm1 - 1) / bm1, mt2 = (rows + bm2 - 1) / bm2;
     // as many tiles of bm1_alt rows cover the segment: use that height
     hb1_s[tid] = bm1_alt > 0 && (int64_t)mt1 * bm1_alt >= rows ? bm1_alt : bm1;
+    hb2_s[tid] = bm2_alt > 0 && (int64_t)mt2 * bm2_alt >= rows ? bm2_alt : bm2;
     c1 = mt1 * (tid < E ? nt1 : nt1s);
     c2 = mt2 * nt2;
     mt1_s[tid] = mt1;
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
       while (g + 1 < nseg && pre[g + 1] <= L) ++g;
       const int local = L - pre[g];
       const int mt = pass == 0 ? mt1_s[g] : mt2_s[g];
-      const int bm = pass == 0 ? hb1_s[g] : bm2;
+      const int bm = pass == 0 ? hb1_s[g] : hb2_s[g];
       const int ncol = (pass == 0 ? (g < E ? nt1 : nt1s) : nt2);
       const int q = local / (kGroupRowTiles * ncol);             // row-tile group (all earlier ones full)
       const int idx = local - q * kGroupRowTiles * ncol;
@@ -107,12 +109,12 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
 }
 
 moe_status launch_build_tile_tables(const moe_cfg* c, const int32_t* offsets, int bm1, int bm1_alt, int nt1,
-                                    int nt1s, TileDesc* t1, int64_t max1, int bm2, int nt2, TileDesc* t2, int64_t max2,
-                                    int32_t* hdr, hipStream_t st) {
+                                    int nt1s, TileDesc* t1, int64_t max1, int bm2, int bm2_alt, int nt2, TileDesc* t2,
+                                    int64_t max2, int32_t* hdr, hipStream_t st) {
   const int64_t most = max1 > max2 ? max1 : max2;
   const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((most + 1023) / 1024, 1), 64);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(blocks), dim3(1024), 0, st, offsets, c->E, c->S, c->T, bm1, bm1_alt,
-                     bm2, nt1, nt1s, nt2, t1, t2, hdr);
+                     bm2, bm2_alt, nt1, nt1s, nt2, t1, t2, hdr);
   return launch_status();
 }
 
@@ -120,7 +122,7 @@ moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
   return launch_build_tile_tables(c, offsets, L.bm1, L.bm1_alt, (int)L.nt1, (int)L.nt1s,
-                                  reinterpret_cast<TileDesc*>(base + L.off_t1), L.max1, L.bm2, (int)L.nt2,
+                                  reinterpret_cast<TileDesc*>(base + L.off_t1), L.max1, L.bm2, L.bm2_alt, (int)L.nt2,
                                   reinterpret_cast<TileDesc*>(base + L.off_t2), L.max2,
                                   reinterpret_cast<int32_t*>(base + L.off_hdr), st);
 }

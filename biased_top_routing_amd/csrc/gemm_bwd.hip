@@ -458,11 +458,11 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   bf16_t* hs = reinterpret_cast<bf16_t*>(base + L.off_hs);
   moe_status s;
   // tables: hdr[0] recompute, hdr[1] dx, hdr[2] dh
-  if ((s = launch_build_tile_tables(c, offsets, kBM1, kBM1Alt, L.nt_re, L.nts_re, t_re, L.max_re, kBwdBM, L.nt_dx,
+  if ((s = launch_build_tile_tables(c, offsets, kBM1, kBM1Alt, L.nt_re, L.nts_re, t_re, L.max_re, kBwdBM, 0, L.nt_dx,
                                     t_dx, L.max_dx, hdr, st)) != MOE_OK)
     return s;
-  if ((s = launch_build_tile_tables(c, offsets, kBwdBM, 0, L.nt_dh, L.nts_dh, t_dh, L.max_dh, kBwdBM, 1, nullptr,
-                                    0, hdr + 2, st)) != MOE_OK)
+  if ((s = launch_build_tile_tables(c, offsets, kBwdBM, 0, L.nt_dh, L.nts_dh, t_dh, L.max_dh, kBwdBM, 0, 1,
+                                    nullptr, 0, hdr + 2, st)) != MOE_OK)
     return s;
   if ((s = launch_gateup_recompute_bf16(c, x_perm, x, w, t_re, hdr, L.max_re, g, u, gs, us, st)) != MOE_OK) return s;
 

@@ -33,13 +33,14 @@ moe_status launch_build_tiles(const moe_cfg* c, const int32_t* offsets, void* ws
 struct TileDesc;
 // Two tables (t1: row height bm1, or bm1_alt for a segment that needs no more
 // tiles of that height (bm1_alt = 0: never), nt1 column tiles per routed
-// segment, nt1s for the shared one; t2: bm2 and nt2 for every segment) and their
+// segment, nt1s for the shared one; t2: bm2 or bm2_alt alike and nt2 for every
+// segment) and their
 // sizes in hdr[0], hdr[1], and the tiles of their routed segments (which come
 // before the shared ones) in hdr[4], hdr[5]; t2 == nullptr builds t1 only
 // (hdr[1] = hdr[5] = 0).  hdr holds at least 8 ints.
 moe_status launch_build_tile_tables(const moe_cfg* c, const int32_t* offsets, int bm1, int bm1_alt, int nt1,
-                                    int nt1s, TileDesc* t1, int64_t max1, int bm2, int nt2, TileDesc* t2, int64_t max2,
-                                    int32_t* hdr, hipStream_t st);
+                                    int nt1s, TileDesc* t1, int64_t max1, int bm2, int bm2_alt, int nt2, TileDesc* t2,
+                                    int64_t max2, int32_t* hdr, hipStream_t st);
 
 // Quantises rows of bf16 values to E4M3 per 1 x 128 tile (sc = amax/448).
 moe_status launch_quantize_rows(const bf16_t* src, int64_t rows, int cols, fp8_t* dst, float* scales,
