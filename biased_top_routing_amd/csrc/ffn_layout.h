@@ -100,6 +100,35 @@ struct TileDesc {
   int32_t seg, row0, rows, nt;
 };
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Grouped GEMM launches: one workgroup per tile of a device-built table that
+// holds ntiles[4] routed tiles followed by the shared-expert ones (ntiles[0] in
+// all).  Each XCD (workgroup id mod 8) takes an equal contiguous share of the
+// shared tiles first, then one of the routed tiles: tiles sharing operands run
+// together in one XCD's L2, and the shared tiles, all full, are spread over
+// every XCD (cut by count alone, the table left the shared tiles to the last
+// XCD, which then finished last).  Returns the table position of this
+// workgroup's tile, or -1 for a surplus workgroup.
+__device__ __forceinline__ int grouped_tile(const int32_t* ntiles) {
+  const int n_real = __builtin_amdgcn_readfirstlane(ntiles[0]);
+  const int n_rt = __builtin_amdgcn_readfirstlane(ntiles[4]);
+  const int per_s = (n_real - n_rt + 7) >> 3, per_r = (n_rt + 7) >> 3;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  if (j < per_s) {
+    const int L = n_rt + xcd * per_s + j;
+    return L < n_real ? L : -1;
+  }
+  const int L = xcd * per_r + (j - per_s);
+  return j - per_s < per_r && L < n_rt ? L : -1;
+}
+#endif
+
+// Workgroups of a grouped launch over a table of at most max_tiles tiles (the
+// two shares of an XCD round up apart: two more per XCD).
+inline int64_t grouped_grid(int64_t max_tiles) {
+  return max_tiles > 0 ? (int64_t)align_up((size_t)max_tiles, 8) + 16 : 0;
+}
+
 struct FfnLayout {
   bool dec;                      // small-batch bf16 configuration
   int bm1, bm2;                  // token rows per tile: gate/up, down

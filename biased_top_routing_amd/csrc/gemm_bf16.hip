@@ -328,23 +328,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     rows = min(BM, p.T - row0);
     nt = blockIdx.y;
   } else {
-    // Each XCD takes an equal share of the shared-expert tiles first, then an
-    // equal share of the routed ones (routed tiles differ in height, shared
-    // ones are all full: cutting the table by count alone left the XCD that
-    // held the shared tiles last to finish).
-    const int n_real = __builtin_amdgcn_readfirstlane(p.ntiles[0]);
-    const int n_rt = __builtin_amdgcn_readfirstlane(p.ntiles[4]);
-    const int per_s = (n_real - n_rt + 7) >> 3, per_r = (n_rt + 7) >> 3;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    int L;
-    if (j < per_s) {
-      L = n_rt + xcd * per_s + j;
-      if (L >= n_real) return;
-    } else {
-      if (j - per_s >= per_r) return;
-      L = xcd * per_r + (j - per_s);
-      if (L >= n_rt) return;
-    }
+    const int L = grouped_tile(p.ntiles);
+    if (L < 0) return;
     const TileDesc d = p.tiles[L];
     // the descriptor is the same for the whole workgroup: keep it in SGPRs
     seg = __builtin_amdgcn_readfirstlane(d.seg);
@@ -362,12 +347,6 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   }
   gemm_tile<MODE, WM, WN, MI, NI, BK, STAGES>(p, lds, seg, row0, rows, nt);
 #endif
-}
-
-// Workgroups of a grouped launch over a table of at most max_tiles tiles: the
-// shared and routed shares of each XCD round up apart (two more per XCD).
-static int64_t grouped_grid(int64_t max_tiles) {
-  return max_tiles > 0 ? (int64_t)align_up((size_t)max_tiles, 8) + 16 : 0;
 }
 
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,

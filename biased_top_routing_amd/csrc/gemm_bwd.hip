@@ -125,12 +125,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
     ldb = p.H;
     b_bytes = p.E * p.H * 2;
   } else if constexpr (!KSEG) {
-    const int n_real = __builtin_amdgcn_readfirstlane(*p.ntiles);
-    const int per = (n_real + 7) >> 3;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
-    if (j >= per) return;
-    const int L = xcd * per + j;
-    if (L >= n_real) return;
+    const int L = grouped_tile(p.ntiles);
+    if (L < 0) return;
     const TileDesc d = p.tiles[L];
     seg = __builtin_amdgcn_readfirstlane(d.seg);
     m0 = __builtin_amdgcn_readfirstlane(d.row0);
@@ -475,14 +471,16 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   p.g_routed = g; p.g_shared = gs; p.u_routed = u; p.u_shared = us;
   p.out_routed = dgu; p.out_shared = dgus; p.h_routed = h; p.h_shared = hs;
   p.tiles = t_dh; p.ntiles = hdr + 2;
-  hipLaunchKernelGGL((gemm_bwd_kernel<kDh, MOE_BWD_TILE>), dim3(grid_of(L.max_dh)), dim3(kBwdThreads), 0, st, p);
+  hipLaunchKernelGGL((gemm_bwd_kernel<kDh, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dh)), dim3(kBwdThreads), 0,
+                     st, p);
   if ((s = launch_status()) != MOE_OK) return s;
   // dx
   p.a_routed = dgu; p.a_shared = dgus;
   p.b_routed = (const bf16_t*)w->w_gate_up; p.b_shared = (const bf16_t*)w->ws_gate_up;
   p.out_routed = dx_perm; p.out_shared = dx_shared;
   p.tiles = t_dx; p.ntiles = hdr + 1;
-  hipLaunchKernelGGL((gemm_bwd_kernel<kDx, MOE_BWD_TILE>), dim3(grid_of(L.max_dx)), dim3(kBwdThreads), 0, st, p);
+  hipLaunchKernelGGL((gemm_bwd_kernel<kDx, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dx)), dim3(kBwdThreads), 0,
+                     st, p);
   if ((s = launch_status()) != MOE_OK) return s;
   // weight gradients
   auto tiles_of = [](int64_t m, int64_t n) {

@@ -132,12 +132,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   const int l16 = lane & 15, g = lane >> 4;
 
   // ------------------------------------------------------------ which tile
-  const int n_real = __builtin_amdgcn_readfirstlane(*p.ntiles);
-  const int per = (n_real + 7) >> 3;
-  const int xcd = blockIdx.x & 7, jj = blockIdx.x >> 3;
-  if (jj >= per) return;
-  const int L = xcd * per + jj;
-  if (L >= n_real) return;
+  const int L = grouped_tile(p.ntiles);
+  if (L < 0) return;
   const TileDesc d = p.tiles[L];
   const int seg = __builtin_amdgcn_readfirstlane(d.seg);
   const int row0 = __builtin_amdgcn_readfirstlane(d.row0);
@@ -425,7 +421,7 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.out_shared = hs; p.out_shared_scale = hss;
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t1);
     p.ntiles = hdr;
-    const int64_t grid = align_up((size_t)L.max1, 8);
+    const int64_t grid = grouped_grid(L.max1);
     if (grid > 0) {
       hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
                          dim3(kThreads8), 0, st, p);
@@ -442,7 +438,7 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.out_shared = y_shared; p.out_shared_scale = nullptr;
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t2);
     p.ntiles = hdr + 1;
-    const int64_t grid = align_up((size_t)L.max2, 8);
+    const int64_t grid = grouped_grid(L.max2);
     if (grid > 0) {
       hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
                          dim3(kThreads8), 0, st, p);
