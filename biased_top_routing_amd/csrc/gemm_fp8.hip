@@ -289,9 +289,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) fb[ni] = frag(base + BM * BK + b_rd[ni] * BK, b_rd[ni], g);
       // row blocks one at a time (short live ranges); the next block's operand
-      // and scale reads are issued before this block's MFMAs
+      // and scale reads are issued before this block's MFMAs, and the previous
+      // block's chunk products are promoted (VALU) under this block's MFMAs
       i32x8_t fa = frag(base + arow0 * BK, arow0, g);
       f32x4_t sa4 = *reinterpret_cast<const f32x4_t*>(sa_st + srow0);
+      f32x4_t prev[NI];
+      float p0[4], p1[4];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         i32x8_t fa_n;
@@ -307,19 +310,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
           s0[r] = sa4[r] * w0;
           s1[r] = sa4[r] * w1;
         }
+        f32x4_t part[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[ni], z, 0, 0, 0, 0, 0, 0);
-          const bool second = MODE == kGateUp8 && ni >= NI / 2;
+          part[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[ni], z, 0, 0, 0, 0, 0, 0);
+          if (mi > 0) {
+            const bool second = MODE == kGateUp8 && ni >= NI / 2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mi][ni][r] = fmaf(part[r], second ? s1[r] : s0[r], acc[mi][ni][r]);
+            for (int r = 0; r < 4; ++r)
+              acc[mi - 1][ni][r] = fmaf(prev[ni][r], second ? p1[r] : p0[r], acc[mi - 1][ni][r]);
+          }
+        }
+        // one MFMA, then the previous block's 4 promotion FMAs of that column block
+        if (mi > 0) {
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) prev[ni] = part[ni];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p0[r] = s0[r];
+          p1[r] = s1[r];
+        }
         if (mi + 1 < MI) {
           fa = fa_n;
           sa4 = sa_n;
         }
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const bool second = MODE == kGateUp8 && ni >= NI / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[MI - 1][ni][r] = fmaf(prev[ni][r], second ? p1[r] : p0[r], acc[MI - 1][ni][r]);
       }
     }
     cur = cur == STAGES - 1 ? 0 : cur + 1;
