@@ -360,7 +360,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
 #undef MOE_ISSUE_BWD
 
   // ------------------------------------------------------------ epilogue
-  // acc[mi][ni][r] = C[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4
+  // acc[mi][ni][r] = C[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  // The weight gradients (45 GB of fp32 at the V3-like shape, never re-read by
+  // this layer) are stored non-temporally: measured 2-5% faster than plain
+  // stores, which also displace the operand panels from the L2.
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -391,12 +394,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
         } else if constexpr (KIND == kDwGu) {
           float* o = shared ? static_cast<float*>(p.out_shared)
                             : static_cast<float*>(p.out_routed) + (int64_t)seg * 2 * p.I * p.H;
-          o[row * N + col] = v;
+          __builtin_nontemporal_store(v, &o[row * N + col]);
         } else if constexpr (KIND == kDwD) {
-          if (shared)
-            static_cast<float*>(p.out_shared)[(int64_t)(col / p.I) * p.H * p.I + row * p.I + col % p.I] = v;
-          else
-            static_cast<float*>(p.out_routed)[(int64_t)seg * p.H * p.I + row * p.I + col] = v;
+          float* o = shared ? static_cast<float*>(p.out_shared) + (int64_t)(col / p.I) * p.H * p.I + col % p.I
+                            : static_cast<float*>(p.out_routed) + (int64_t)seg * p.H * p.I + col;
+          __builtin_nontemporal_store(v, &o[row * p.I]);
         } else {
           static_cast<float*>(p.out_routed)[(int64_t)split * p.E * p.H + row * N + col] = v;
         }
