@@ -17,8 +17,9 @@
 // the BN/2 up rows of the same intermediate columns, each wavefront holding
 // matching gate and up blocks, so SwiGLU is applied in registers.
 // Grouped tiles come from a device-built table (segment, first row, rows,
-// column tile); the table is cut into 8 contiguous ranges, one per XCD
-// (workgroup id mod 8), so tiles sharing operands run together in one XCD's L2.
+// column tile); each XCD (workgroup id mod 8) takes a contiguous share of its
+// shared-expert tiles and one of its routed tiles, so tiles sharing operands
+// run together in one XCD's L2.
 #include "common.h"
 #include "ffn_layout.h"
 #include "gemm_common.h"
@@ -349,6 +350,66 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
 #endif
 }
 
+// Router GEMM for small batches, whose token-tile grid would leave most CUs
+// idle (decode: T = 128 gives two 64-token tiles, each walking all of K):
+// a workgroup computes a TM x TN tile of (tokens, experts) with MFMA blocks of
+// TM x TN (32 x 32 x 16 or 16 x 16 x 32 bf16), each of its 16 wavefronts takes
+// one sixteenth of K straight from memory into operand registers (no operand is
+// shared between wavefronts, so nothing is staged in LDS), and the 16 partial
+// tiles are added through LDS in wavefront order (a fixed order: repeated calls
+// give identical bits; the summation order, and so the last bits of the
+// affinities, differ from the large-batch tiles).  Token and expert rows past
+// the ends are clamped to the last valid row and their results not stored.
+constexpr int kRsWaves = 16;
+template <int TM>   // 32: 32 x 32 x 16 blocks; 16: 16 x 16 x 32 blocks
+__global__ __launch_bounds__(64 * kRsWaves) void router_splitk_kernel(const bf16_t* __restrict__ x,
+                                                                     const bf16_t* __restrict__ w,
+                                                                     const float* __restrict__ offset,
+                                                                     float* __restrict__ scores, int T, int H,
+                                                                     int E) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NR = TM * TM / 64;       // accumulator values per lane
+  constexpr int KS = 512 / TM;           // K per MFMA step (16 or 32)
+  __shared__ float red[kRsWaves][NR][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane % TM, kg = lane / TM;
+  const int t0 = blockIdx.x * TM, e0 = blockIdx.y * TM;
+  // operand lane l: row l % TM, K elements 8 (l / TM) .. + 7 of each step
+  const bf16_t* xa = x + (int64_t)min(t0 + lr, T - 1) * H + 8 * kg;
+  const bf16_t* wb = w + (int64_t)min(e0 + lr, E - 1) * H + 8 * kg;
+  const int nks = H / KS;
+  const int ks0 = wave * nks / kRsWaves, ks1 = (wave + 1) * nks / kRsWaves;
+  typedef float accv_t __attribute__((ext_vector_type(NR)));
+  accv_t acc;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+#pragma unroll 4
+  for (int ks = ks0; ks < ks1; ++ks) {
+    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xa + ks * KS);
+    const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(wb + ks * KS);
+    if constexpr (TM == 32) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) red[wave][r][lane] = acc[r];
+  __syncthreads();
+  for (int q = threadIdx.x; q < NR * 64; q += 64 * kRsWaves) {
+    const int r = q >> 6, l = q & 63;
+    float sum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kRsWaves; ++v) sum += red[v][r][l];
+    // acc[r] of lane l: 32 x 32 blocks row 8 (r / 4) + 4 (l / 32) + r % 4;
+    // 16 x 16 blocks row 4 (l / 16) + r; column l % TM
+    const int i = TM == 32 ? 8 * (r >> 2) + 4 * (l >> 5) + (r & 3) : 4 * (l >> 4) + r;
+    const int t = t0 + i, e = e0 + l % TM;
+    if (t < T && e < E) {
+      const float lg = sum + (offset ? offset[e] : 0.f);
+      scores[(int64_t)t * E + e] = 1.0f / (1.0f + expf(-lg));
+    }
+  }
+#endif
+}
+
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
                               const float* offset, float* scores, hipStream_t st) {
   GemmParams p{};
@@ -357,11 +418,11 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   p.offset = offset;
   p.out_routed = scores;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-  // Every token tile re-reads its columns of the router weight from L2, so the
-  // tile is as large as the batch allows while the grid still covers every CU:
-  // 256 x 256 and 128 x 256 for large batches, 128 x 128 at T = 16384 (two
-  // column tiles of 128 experts: 3.5 instead of 4.6 MB of operand loads per tile
-  // against 64 x 256, measured 14% faster), else 64 x 256.
+  // Large batches: every token tile re-reads its columns of the router weight
+  // from L2, so the tile is as large as the batch allows while the grid still
+  // covers every CU: 256 x 256 and 128 x 256 for large batches, 128 x 128 at
+  // T = 16384 (two column tiles of 128 experts: 3.5 instead of 4.6 MB of operand
+  // loads per tile against 64 x 256, measured 14% faster), else 64 x 256.
   static int n_cu = 0;
   if (n_cu == 0) {
     int dev = 0, n = 0;
@@ -383,7 +444,19 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
   using RT256 = TileCfg<MOE_RT256_TILE>;
   using RT128 = TileCfg<MOE_RT128_TILE>;
   using RT128N = TileCfg<MOE_RT128N_TILE>;
-  if (tiles(RT256{}) >= n_cu) launch(RT256{});
+  // Small batches: the split-K kernel with 16 x 16 tiles while there are at
+  // most two per CU, else with 32 x 32 tiles while there are at most two per CU
+  // (route stage with a cache flush, against 64 x 256 tiles: E = 256, T = 128
+  // 100 -> 27 us, T = 2048 99 -> 82 us; E = 64, T = 4096 33 -> 23 us).
+  const int64_t t16 = ((int64_t)c->T + 15) / 16 * ((c->E + 15) / 16);
+  const int64_t t32 = ((int64_t)c->T + 31) / 32 * ((c->E + 31) / 32);
+  if (t16 <= 2 * n_cu)
+    hipLaunchKernelGGL(router_splitk_kernel<16>, dim3((unsigned)((c->T + 15) / 16), (unsigned)((c->E + 15) / 16)),
+                       dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
+  else if (t32 <= 2 * n_cu)
+    hipLaunchKernelGGL(router_splitk_kernel<32>, dim3((unsigned)((c->T + 31) / 32), (unsigned)((c->E + 31) / 32)),
+                       dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
+  else if (tiles(RT256{}) >= n_cu) launch(RT256{});
   else if (tiles(RT128{}) >= n_cu) launch(RT128{});
   else if (tiles(RT128N{}) >= n_cu) launch(RT128N{});
   else launch(TileCfg<MOE_RT_TILE>{});
