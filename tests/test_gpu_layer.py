@@ -215,11 +215,11 @@ def test_layer_determinism_and_routing_invariants():
     np.testing.assert_allclose(w, c.route_scale * sel / sel.sum(1, keepdims=True), rtol=2e-6, atol=0)
 
 
-@pytest.mark.parametrize("T,E", [(128, 256), (300, 200), (1000, 256), (8192, 256), (16384, 256), (16384, 192),
+@pytest.mark.parametrize("T,E", [(1, 256), (128, 256), (300, 200), (1000, 256), (8192, 256), (16384, 256), (16384, 192),
                                  (32768, 64), (65613, 64)])
 def test_router_gemm_tile_heights(T, E):
     """The router GEMM's kernel and tile follow the batch on a 256-CU chip: the
-    split-K kernel with 16 x 16 tiles (T = 128; T = 300 with ragged token and
+    split-K kernel with 16 x 16 tiles (T = 1, 128; T = 300 with ragged token and
     expert tiles) and 32 x 32 tiles (T = 1000), then 64 x 256 (T = 8192), 128 x 128
     (T = 16384 with two column tiles of experts, the second ragged for E = 192),
     128 x 256 and 256 x 256 (the last with a ragged final row tile): affinities
