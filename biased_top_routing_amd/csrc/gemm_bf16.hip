@@ -19,7 +19,9 @@
 // Grouped tiles come from a device-built table (segment, first row, rows,
 // column tile); each XCD (workgroup id mod 8) takes a contiguous share of its
 // shared-expert tiles and one of its routed tiles, so tiles sharing operands
-// run together in one XCD's L2.
+// run together in one XCD's L2.  A gate/up tile whose rows fit fewer padded
+// MFMA rows with MI_ALT row blocks per wavefront runs that body instead.
+// Small batches route through a separate split-K router kernel (no LDS ring).
 #include "common.h"
 #include "ffn_layout.h"
 #include "gemm_common.h"
