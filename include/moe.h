@@ -100,6 +100,9 @@ typedef struct {
  * Groups are chosen first (the M largest group scores, ties to the lower group),
  * then the k largest s + b among the experts of the chosen groups.
  * NaN scores give unspecified indices.
+ * The router GEMM sums in a fixed order per batch size (repeated calls give
+ * identical bits); small and large batches use different kernels, so the last
+ * bits of a token's affinities can depend on T.
  */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
                      const float* logit_offset, const float* bias, float* scores,
