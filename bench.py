@@ -221,7 +221,10 @@ BWD_STAGES = ["combine_bwd", "expert_ffn_bwd", "route_bwd", "dispatch_bwd"]
 def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
     """One training step of the layer at the prefill shape: the forward pass (with the
     row copy, whose x_perm the backward reads) and the backward pass (gradients of
-    every weight, the input and the balance loss).  Per-call times from HIP events."""
+    every weight, the input and the balance loss).  Per-call times from HIP events.
+    The main figures keep the gate and up outputs in the forward pass
+    (moe_expert_ffn_save, 2 (T k + T S) I bf16 values) so that the backward pass
+    starts from them; "recompute" times the same step recomputing them instead."""
     import numpy as np
     import torch
 
@@ -229,7 +232,7 @@ def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
     from biased_top_routing_amd.runner import MoeLayerGPU
     from workloads.inputs import make_x
 
-    layer = MoeLayerGPU(c, w, gather=False)
+    layer = MoeLayerGPU(c, w, gather=False, save_gu=True)
     x = to_dev(make_x(c, 0))
     g = torch.Generator(device="cuda").manual_seed(5)
     dy = torch.randn((c.T, c.H), device="cuda", generator=g).to(torch.bfloat16)
@@ -237,18 +240,23 @@ def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
     layer.alloc_backward()
     cfg = layer.cfg
 
-    def bwd_calls():
-        return [lambda: L.moe_combine_backward(cfg, dy, layer.y_perm, layer.inv, layer.topk_w, layer.dy_perm,
-                                               layer.d_topk_w),
-                lambda: L.moe_expert_ffn_backward(cfg, layer.x_perm, x, layer.offsets, layer.weights, layer.dy_perm,
-                                                  dy, layer.dx_perm, layer.dx_shared, layer.grads, layer.ws_ffn_bwd),
-                lambda: L.moe_route_backward(cfg, x, layer.w_router, layer.scores, layer.topk_idx, layer.d_topk_w,
-                                             alpha, seq_len, layer.dx_router, layer.g_w_router, layer.loss_bal,
-                                             layer.ws_route_bwd),
-                lambda: L.moe_dispatch_backward(cfg, layer.dx_perm, layer.dx_shared, layer.dx_router, layer.inv,
-                                                layer.dx)]
+    def ffn_bwd():
+        if layer.save_gu:
+            L.moe_expert_ffn_backward_saved(cfg, layer.x_perm, x, layer.offsets, layer.weights, layer.saved,
+                                            layer.dy_perm, dy, layer.dx_perm, layer.dx_shared, layer.grads,
+                                            layer.ws_ffn_bwd)
+        else:
+            L.moe_expert_ffn_backward(cfg, layer.x_perm, x, layer.offsets, layer.weights, layer.dy_perm, dy,
+                                      layer.dx_perm, layer.dx_shared, layer.grads, layer.ws_ffn_bwd)
 
-    calls = bwd_calls()
+    calls = [lambda: L.moe_combine_backward(cfg, dy, layer.y_perm, layer.inv, layer.topk_w, layer.dy_perm,
+                                            layer.d_topk_w),
+             ffn_bwd,
+             lambda: L.moe_route_backward(cfg, x, layer.w_router, layer.scores, layer.topk_idx, layer.d_topk_w,
+                                          alpha, seq_len, layer.dx_router, layer.g_w_router, layer.loss_bal,
+                                          layer.ws_route_bwd),
+             lambda: L.moe_dispatch_backward(cfg, layer.dx_perm, layer.dx_shared, layer.dx_router, layer.inv,
+                                             layer.dx)]
 
     def step(ev=None):
         if ev is not None:
@@ -261,29 +269,40 @@ def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
         if ev is not None:
             ev[len(calls) + 1].record()
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    fwd = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
-    st = {n: float(np.mean([ev[j + 1].elapsed_time(ev[j + 2]) for ev in events])) for j, n in enumerate(BWD_STAGES)}
+    def timed():
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 2)] for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        fwd = float(np.mean([ev[0].elapsed_time(ev[1]) for ev in events]))
+        st = {n: float(np.mean([ev[j + 1].elapsed_time(ev[j + 2]) for ev in events]))
+              for j, n in enumerate(BWD_STAGES)}
+        return wall, fwd, st
+
     rows = c.T * (c.k + c.S)
-    ffn_bwd_flops = 16 * c.H * c.I * rows            # recomputed gate/up 4HI, dh 2HI, dx 4HI, dW_gu 4HI, dW_d 2HI
+    ffn_bwd_flops = 12 * c.H * c.I * rows            # dh 2HI, dx 4HI, dW_gu 4HI, dW_d 2HI per row
     router_bwd_flops = 4 * c.T * c.E * c.H
     fwd_flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
+    wall, fwd, st = timed()
     ffn_tf = ffn_bwd_flops / (st["expert_ffn_bwd"] * 1e-3) / 1e12
     out = {"workload": "v3_prefill_train_bf16", "T": c.T, "alpha": alpha, "seq_len": seq_len,
+           "gate_up_outputs_kept": True,
            "ms_per_step": round(wall, 4), "tokens_per_s": round(c.T / (wall * 1e-3), 1),
            "forward_ms": round(fwd, 4), "backward_ms": round(sum(st.values()), 4),
            "backward_stages_ms": {k: round(v, 4) for k, v in st.items()},
            "expert_ffn_bwd_tflops": round(ffn_tf, 2), "expert_ffn_bwd_frac_of_peak": round(ffn_tf / PEAK_BF16_TFLOPS, 4),
            "step_tflops": round((fwd_flops + ffn_bwd_flops + router_bwd_flops) / (wall * 1e-3) / 1e12, 2),
            "loss_bal": float(layer.loss_bal.item())}
+    layer.save_gu = False                            # the same step recomputing g, u in the backward pass
+    wall_r, fwd_r, st_r = timed()
+    out["recompute"] = {"ms_per_step": round(wall_r, 4), "forward_ms": round(fwd_r, 4),
+                        "backward_ms": round(sum(st_r.values()), 4),
+                        "expert_ffn_bwd_ms": round(st_r["expert_ffn_bwd"], 4)}
     del layer, x, dy
     torch.cuda.empty_cache()
     return out

@@ -46,6 +46,10 @@ class MoeExpertGrads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_gate_up", "w_down", "ws_gate_up", "ws_down")]
 
 
+class MoeFfnSaved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("g", "u", "gs", "us")]
+
+
 _lib = None
 
 
@@ -65,10 +69,15 @@ def lib() -> ctypes.CDLL:
                                ctypes.c_int, vp],
             "moe_expert_ffn_gather": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, sz,
                                       ctypes.c_int, vp],
+            "moe_expert_ffn_save": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp,
+                                    ctypes.POINTER(MoeFfnSaved), vp, sz, ctypes.c_int, vp],
             "moe_combine": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_combine_backward": [cfgp, vp, vp, vp, vp, vp, vp, vp],
             "moe_expert_ffn_backward": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp,
                                         ctypes.POINTER(MoeExpertGrads), vp, sz, vp],
+            "moe_expert_ffn_backward_saved": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights),
+                                              ctypes.POINTER(MoeFfnSaved), vp, vp, vp, vp,
+                                              ctypes.POINTER(MoeExpertGrads), vp, sz, vp],
             "moe_route_backward": [cfgp, vp, vp, vp, vp, vp, f32, i32, vp, vp, vp, vp, sz, vp],
             "moe_dispatch_backward": [cfgp, vp, vp, vp, vp, vp, vp],
             "moe_update_bias": [cfgp, vp, vp, f32, vp],
@@ -170,6 +179,17 @@ def moe_expert_ffn_gather(cfg, x, perm, offsets, weights: MoeExpertWeights, y_pe
         _p(ws), _nbytes(ws), phase, _s(stream)))
 
 
+def ffn_saved(g, u, gs=None, us=None) -> MoeFfnSaved:
+    return MoeFfnSaved(_p(g), _p(u), _p(gs), _p(us))
+
+
+def moe_expert_ffn_save(cfg, x_perm, perm, offsets, weights: MoeExpertWeights, x, y_perm, y_shared,
+                        saved: MoeFfnSaved, ws, phase=MOE_FFN_ALL, stream=None):
+    _check("moe_expert_ffn_save", lib().moe_expert_ffn_save(
+        ctypes.byref(cfg), _p(x_perm), _p(perm), _p(offsets), ctypes.byref(weights), _p(x), _p(y_perm),
+        _p(y_shared), ctypes.byref(saved), _p(ws), _nbytes(ws), phase, _s(stream)))
+
+
 def moe_combine(cfg, y_perm, y_shared, inv, topk_w, y, stream=None):
     _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _p(y_perm), _p(y_shared), _p(inv), _p(topk_w),
                                             _p(y), _s(stream)))
@@ -189,6 +209,13 @@ def moe_expert_ffn_backward(cfg, x_perm, x, offsets, weights: MoeExpertWeights, 
     _check("moe_expert_ffn_backward", lib().moe_expert_ffn_backward(
         ctypes.byref(cfg), _p(x_perm), _p(x), _p(offsets), ctypes.byref(weights), _p(dy_perm), _p(dy), _p(dx_perm),
         _p(dx_shared), ctypes.byref(grads), _p(ws), _nbytes(ws), _s(stream)))
+
+
+def moe_expert_ffn_backward_saved(cfg, x_perm, x, offsets, weights: MoeExpertWeights, saved: MoeFfnSaved, dy_perm,
+                                  dy, dx_perm, dx_shared, grads: MoeExpertGrads, ws, stream=None):
+    _check("moe_expert_ffn_backward_saved", lib().moe_expert_ffn_backward_saved(
+        ctypes.byref(cfg), _p(x_perm), _p(x), _p(offsets), ctypes.byref(weights), ctypes.byref(saved), _p(dy_perm),
+        _p(dy), _p(dx_perm), _p(dx_shared), ctypes.byref(grads), _p(ws), _nbytes(ws), _s(stream)))
 
 
 def moe_route_backward(cfg, x, w_router, scores, topk_idx, d_topk_w, alpha, seq_len, dx_router, dw_router, loss, ws,

@@ -260,11 +260,13 @@ extern "C" moe_status moe_combine_backward(const moe_cfg* cfg, const void* dy, c
   return launch_status();
 }
 
-extern "C" moe_status moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const void* x,
-                                              const int32_t* offsets, const moe_expert_weights* w,
-                                              const void* dy_perm, const void* dy, void* dx_perm, void* dx_shared,
-                                              const moe_expert_grads* grads, void* ws, size_t ws_bytes,
-                                              void* stream) {
+namespace {
+
+// Both expert backward entry points; saved == nullptr: recompute g, u.
+moe_status expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const void* x, const int32_t* offsets,
+                               const moe_expert_weights* w, const moe_ffn_saved* saved, const void* dy_perm,
+                               const void* dy, void* dx_perm, void* dx_shared, const moe_expert_grads* grads,
+                               void* ws, size_t ws_bytes, void* stream) {
   moe_status st = validate_cfg(cfg);
   if (st != MOE_OK) return st;
   if (!bwd_dtypes_ok(cfg)) return MOE_ERR_UNSUPPORTED;
@@ -275,10 +277,33 @@ extern "C" moe_status moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_
   const int64_t widest = std::max<int64_t>(cfg->H, 2LL * std::max(cfg->S, 1) * cfg->I);
   if ((int64_t)cfg->T * widest * 2 > INT32_MAX || 2LL * cfg->S * cfg->I * cfg->H * 2 > INT32_MAX)
     return MOE_ERR_UNSUPPORTED;
+  if (saved && (!saved->g || !saved->u || (cfg->S > 0 && (!saved->gs || !saved->us)))) return MOE_ERR_NULL;
   if (ws_bytes < FfnBwdLayout(cfg).total) return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
-  return launch_ffn_bwd_bf16(cfg, (const bf16_t*)x_perm, (const bf16_t*)x, offsets, w, (const bf16_t*)dy_perm,
-                             (const bf16_t*)dy, (bf16_t*)dx_perm, (bf16_t*)dx_shared, grads, ws, as_stream(stream));
+  return launch_ffn_bwd_bf16(cfg, (const bf16_t*)x_perm, (const bf16_t*)x, offsets, w, saved,
+                             (const bf16_t*)dy_perm, (const bf16_t*)dy, (bf16_t*)dx_perm, (bf16_t*)dx_shared, grads,
+                             ws, as_stream(stream));
+}
+
+}  // namespace
+
+extern "C" moe_status moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const void* x,
+                                              const int32_t* offsets, const moe_expert_weights* w,
+                                              const void* dy_perm, const void* dy, void* dx_perm, void* dx_shared,
+                                              const moe_expert_grads* grads, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  return expert_ffn_backward(cfg, x_perm, x, offsets, w, nullptr, dy_perm, dy, dx_perm, dx_shared, grads, ws,
+                             ws_bytes, stream);
+}
+
+extern "C" moe_status moe_expert_ffn_backward_saved(const moe_cfg* cfg, const void* x_perm, const void* x,
+                                                    const int32_t* offsets, const moe_expert_weights* w,
+                                                    const moe_ffn_saved* saved, const void* dy_perm, const void* dy,
+                                                    void* dx_perm, void* dx_shared, const moe_expert_grads* grads,
+                                                    void* ws, size_t ws_bytes, void* stream) {
+  if (!saved) return MOE_ERR_NULL;
+  return expert_ffn_backward(cfg, x_perm, x, offsets, w, saved, dy_perm, dy, dx_perm, dx_shared, grads, ws,
+                             ws_bytes, stream);
 }
 
 extern "C" moe_status moe_route_backward(const moe_cfg* cfg, const void* x, const void* w_router,

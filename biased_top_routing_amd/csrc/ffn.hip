@@ -231,8 +231,8 @@ namespace {
 // gathered from x through perm.
 moe_status expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_perm_scale,
                       const int32_t* perm, const int32_t* offsets, const moe_expert_weights* w,
-                      const void* x, void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
-                      void* stream) {
+                      const void* x, void* y_perm, void* y_shared, const moe_ffn_saved* saved, void* ws,
+                      size_t ws_bytes, int phase, void* stream) {
   moe_status st = validate_cfg(cfg);
   if (st != MOE_OK) return st;
   if (phase != MOE_FFN_ALL && phase != MOE_FFN_GATE_UP && phase != MOE_FFN_DOWN)
@@ -245,6 +245,10 @@ moe_status expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_per
   const bool fp8 = cfg->wgt == MOE_FP8_E4M3;
   if (fp8 && ((!perm && !x_perm_scale) || !w->w_gate_up_scale || !w->w_down_scale)) return MOE_ERR_NULL;
   if (fp8 && cfg->S > 0 && (!w->ws_gate_up_scale || !w->ws_down_scale)) return MOE_ERR_NULL;
+  if (saved) {
+    if (cfg->act != MOE_BF16 || cfg->wgt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (!saved->g || !saved->u || (cfg->S > 0 && (!saved->gs || !saved->us))) return MOE_ERR_NULL;
+  }
   // gathered rows are addressed by 32-bit byte offsets into x (one row past
   // the end marks a dropped row)
   if (perm && cfg->act != MOE_F32 &&
@@ -258,7 +262,8 @@ moe_status expert_ffn(const moe_cfg* cfg, const void* x_perm, const float* x_per
                           (float*)y_shared, ws, phase, s);
   if (!fp8)
     return launch_ffn_bf16(cfg, (const bf16_t*)x_perm, perm, offsets, w, (const bf16_t*)x,
-                           (bf16_t*)y_perm, (bf16_t*)y_shared, ws, phase, s);
+                           (bf16_t*)y_perm, (bf16_t*)y_shared, phase == MOE_FFN_DOWN ? nullptr : saved, ws,
+                           phase, s);
   return launch_ffn_fp8(cfg, (const fp8_t*)x_perm, x_perm_scale, perm, offsets, w, (const bf16_t*)x,
                         (bf16_t*)y_perm, (bf16_t*)y_shared, ws, phase, s);
 }
@@ -270,7 +275,7 @@ extern "C" moe_status moe_expert_ffn(const moe_cfg* cfg, const void* x_perm, con
                                      void* y_perm, void* y_shared, void* ws, size_t ws_bytes, int phase,
                                      void* stream) {
   if (!x_perm) return MOE_ERR_NULL;
-  return expert_ffn(cfg, x_perm, x_perm_scale, nullptr, offsets, w, x, y_perm, y_shared, ws, ws_bytes,
+  return expert_ffn(cfg, x_perm, x_perm_scale, nullptr, offsets, w, x, y_perm, y_shared, nullptr, ws, ws_bytes,
                     phase, stream);
 }
 
@@ -279,6 +284,15 @@ extern "C" moe_status moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, c
                                             void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
                                             int phase, void* stream) {
   if (!perm) return MOE_ERR_NULL;
-  return expert_ffn(cfg, nullptr, nullptr, perm, offsets, w, x, y_perm, y_shared, ws, ws_bytes, phase,
+  return expert_ffn(cfg, nullptr, nullptr, perm, offsets, w, x, y_perm, y_shared, nullptr, ws, ws_bytes, phase,
                     stream);
+}
+
+extern "C" moe_status moe_expert_ffn_save(const moe_cfg* cfg, const void* x_perm, const int32_t* perm,
+                                          const int32_t* offsets, const moe_expert_weights* w, const void* x,
+                                          void* y_perm, void* y_shared, const moe_ffn_saved* saved, void* ws,
+                                          size_t ws_bytes, int phase, void* stream) {
+  if (!saved || (!x_perm && !perm)) return MOE_ERR_NULL;
+  return expert_ffn(cfg, x_perm, nullptr, x_perm ? nullptr : perm, offsets, w, x, y_perm, y_shared, saved, ws,
+                    ws_bytes, phase, stream);
 }

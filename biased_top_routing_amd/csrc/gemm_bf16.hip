@@ -30,9 +30,10 @@
 namespace moe {
 
 // kGateUpGU: the gate/up GEMM storing the gate and up outputs themselves
-// (recomputed for the backward pass) instead of h.
-enum { kRouter = 0, kGateUp = 1, kDown = 2, kGateUpGU = 3 };
-constexpr bool is_gate_up(int mode) { return mode == kGateUp || mode == kGateUpGU; }
+// (recomputed for the backward pass) instead of h; kGateUpSave: storing h and
+// the gate and up outputs (a forward pass that keeps them for the backward).
+enum { kRouter = 0, kGateUp = 1, kDown = 2, kGateUpGU = 3, kGateUpSave = 4 };
+constexpr bool is_gate_up(int mode) { return mode == kGateUp || mode == kGateUpGU || mode == kGateUpSave; }
 
 
 struct GemmParams {
@@ -41,10 +42,12 @@ struct GemmParams {
   const bf16_t* w_routed;   // gate/up: w_gate_up; down: w_down; router: w_router
   const bf16_t* w_shared;   // gate/up: ws_gate_up; down: ws_down
   const float* offset;      // router logit offset (nullable)
-  void* out_routed;         // gate/up: h_perm; down: y_perm; router: scores (fp32); gate/up GU: gate
-  void* out_shared;         // gate/up: h_shared; down: y_shared; gate/up GU: gate
-  void* out2_routed;        // gate/up GU: up outputs
-  void* out2_shared;
+  void* out_routed;         // gate/up: h_perm; down: y_perm; router: scores (fp32)
+  void* out_shared;         // gate/up: h_shared; down: y_shared
+  bf16_t* g_routed;         // gate/up GU and save: gate outputs [rows, I]
+  bf16_t* u_routed;         //   up outputs
+  bf16_t* g_shared;         //   shared experts' [T, S*I]
+  bf16_t* u_shared;
   const TileDesc* tiles;
   const int32_t* ntiles;
   const int32_t* perm;      // gate/up: non-null -> routed rows gathered from a_shared
@@ -269,26 +272,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
       const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (i >= rows) continue;
       const int64_t row = row0 + i;
-      if constexpr (MODE == kGateUp) {
+      if constexpr (is_gate_up(MODE)) {
         constexpr int HALF = NI / 2;
         bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+        bf16_t* og = shared ? p.g_shared : p.g_routed;
+        bf16_t* ou = shared ? p.u_shared : p.u_routed;
 #pragma unroll
         for (int ni = 0; ni < HALF; ++ni) {
           const int col = nt * (BN / 2) + wn * HALF * 32 + ni * 32 + lr;
           const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
-          const float h = g / (1.0f + __expf(-g)) * u;
-          if (col < ncols) out[row * ncols + col] = f32_to_bf16(h);
-        }
-      } else if constexpr (MODE == kGateUpGU) {
-        constexpr int HALF = NI / 2;
-        bf16_t* og = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
-        bf16_t* ou = static_cast<bf16_t*>(shared ? p.out2_shared : p.out2_routed);
-#pragma unroll
-        for (int ni = 0; ni < HALF; ++ni) {
-          const int col = nt * (BN / 2) + wn * HALF * 32 + ni * 32 + lr;
           if (col < ncols) {
-            og[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
-            ou[row * ncols + col] = f32_to_bf16(acc[mi][ni + HALF][r]);
+            if constexpr (MODE != kGateUpGU) out[row * ncols + col] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+            if constexpr (MODE != kGateUp) {
+              og[row * ncols + col] = f32_to_bf16(g);
+              ou[row * ncols + col] = f32_to_bf16(u);
+            }
           }
         }
       } else if constexpr (MODE == kDown) {
@@ -467,7 +465,8 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
 
 moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t* perm,
                            const int32_t* offsets, const moe_expert_weights* w, const bf16_t* x,
-                           bf16_t* y_perm, bf16_t* y_shared, void* ws, int phase, hipStream_t st) {
+                           bf16_t* y_perm, bf16_t* y_shared, const moe_ffn_saved* saved, void* ws, int phase,
+                           hipStream_t st) {
   const FfnLayout L(c);
   char* base = static_cast<char*>(ws);
   const int32_t* hdr = reinterpret_cast<const int32_t*>(base + L.off_hdr);
@@ -483,15 +482,20 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t1);
     p.ntiles = hdr;
     p.perm = perm;
+    if (saved) {
+      p.g_routed = static_cast<bf16_t*>(saved->g); p.u_routed = static_cast<bf16_t*>(saved->u);
+      p.g_shared = static_cast<bf16_t*>(saved->gs); p.u_shared = static_cast<bf16_t*>(saved->us);
+    }
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
     const int64_t grid = grouped_grid(L.max1);
     if (grid > 0) {
-      if (L.dec)
-        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_DEC_GU_TILE>), dim3((unsigned)grid),
-                           dim3(64 * DecGateUpTile::WM * DecGateUpTile::WN), 0, st, p);
-      else
-        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE, MOE_GU_MI_ALT>), dim3((unsigned)grid),
-                           dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);
+      const dim3 dg((unsigned)grid), bd(64 * DecGateUpTile::WM * DecGateUpTile::WN),
+          bg(64 * GateUpTile::WM * GateUpTile::WN);
+      if (L.dec && saved) hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpSave, MOE_DEC_GU_TILE>), dg, bd, 0, st, p);
+      else if (L.dec) hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_DEC_GU_TILE>), dg, bd, 0, st, p);
+      else if (saved)
+        hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpSave, MOE_GU_TILE, MOE_GU_MI_ALT>), dg, bg, 0, st, p);
+      else hipLaunchKernelGGL((gemm_bf16_kernel<kGateUp, MOE_GU_TILE, MOE_GU_MI_ALT>), dg, bg, 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -524,8 +528,8 @@ moe_status launch_gateup_recompute_bf16(const moe_cfg* c, const bf16_t* x_perm, 
   GemmParams p{};
   p.a_routed = x_perm; p.a_shared = x;
   p.w_routed = (const bf16_t*)w->w_gate_up; p.w_shared = (const bf16_t*)w->ws_gate_up;
-  p.out_routed = g; p.out2_routed = u;
-  p.out_shared = gs; p.out2_shared = us;
+  p.g_routed = g; p.u_routed = u;
+  p.g_shared = gs; p.u_shared = us;
   p.tiles = tiles;
   p.ntiles = ntiles;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;

@@ -437,19 +437,20 @@ using WgTile = BwdTile<MOE_BWD_WG_TILE>;
 static inline unsigned grid_of(int64_t n) { return (unsigned)align_up((size_t)(n > 0 ? n : 0), 8); }
 
 moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf16_t* x, const int32_t* offsets,
-                               const moe_expert_weights* w, const bf16_t* dy_perm, const bf16_t* dy,
-                               bf16_t* dx_perm, bf16_t* dx_shared, const moe_expert_grads* gr, void* ws,
-                               hipStream_t st) {
+                               const moe_expert_weights* w, const moe_ffn_saved* saved, const bf16_t* dy_perm,
+                               const bf16_t* dy, bf16_t* dx_perm, bf16_t* dx_shared, const moe_expert_grads* gr,
+                               void* ws, hipStream_t st) {
   const FfnBwdLayout L(c);
   char* base = static_cast<char*>(ws);
   int32_t* hdr = reinterpret_cast<int32_t*>(base + L.off_hdr);
   TileDesc* t_re = reinterpret_cast<TileDesc*>(base + L.off_tre);
   TileDesc* t_dh = reinterpret_cast<TileDesc*>(base + L.off_tdh);
   TileDesc* t_dx = reinterpret_cast<TileDesc*>(base + L.off_tdx);
-  bf16_t* g = reinterpret_cast<bf16_t*>(base + L.off_g);
-  bf16_t* u = reinterpret_cast<bf16_t*>(base + L.off_u);
-  bf16_t* gs = reinterpret_cast<bf16_t*>(base + L.off_gs);
-  bf16_t* us = reinterpret_cast<bf16_t*>(base + L.off_us);
+  // the gate and up outputs: kept by the forward pass, or recomputed here
+  bf16_t* g = saved ? static_cast<bf16_t*>(saved->g) : reinterpret_cast<bf16_t*>(base + L.off_g);
+  bf16_t* u = saved ? static_cast<bf16_t*>(saved->u) : reinterpret_cast<bf16_t*>(base + L.off_u);
+  bf16_t* gs = saved ? static_cast<bf16_t*>(saved->gs) : reinterpret_cast<bf16_t*>(base + L.off_gs);
+  bf16_t* us = saved ? static_cast<bf16_t*>(saved->us) : reinterpret_cast<bf16_t*>(base + L.off_us);
   bf16_t* dgu = reinterpret_cast<bf16_t*>(base + L.off_dgu);
   bf16_t* dgus = reinterpret_cast<bf16_t*>(base + L.off_dgus);
   bf16_t* h = reinterpret_cast<bf16_t*>(base + L.off_h);
@@ -462,7 +463,8 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   if ((s = launch_build_tile_tables(c, offsets, kBwdBM, 0, L.nt_dh, L.nts_dh, t_dh, L.max_dh, kBwdBM, 0, 1,
                                     nullptr, 0, hdr + 2, st)) != MOE_OK)
     return s;
-  if ((s = launch_gateup_recompute_bf16(c, x_perm, x, w, t_re, hdr, L.max_re, g, u, gs, us, st)) != MOE_OK) return s;
+  if (!saved && (s = launch_gateup_recompute_bf16(c, x_perm, x, w, t_re, hdr, L.max_re, g, u, gs, us, st)) != MOE_OK)
+    return s;
 
   BwdParams p{};
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;

@@ -13,10 +13,12 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
 
 // x_perm: the expert-sorted rows written by dispatch; or perm != nullptr: the
 // routed gate/up rows are gathered from x (row p = token perm[p] / k) and
-// x_perm is not read.
+// x_perm is not read.  saved != nullptr: the gate/up GEMM also stores its gate
+// and up outputs there.
 moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t* perm,
                            const int32_t* offsets, const moe_expert_weights* w, const bf16_t* x,
-                           bf16_t* y_perm, bf16_t* y_shared, void* ws, int phase, hipStream_t st);
+                           bf16_t* y_perm, bf16_t* y_shared, const moe_ffn_saved* saved, void* ws, int phase,
+                           hipStream_t st);
 
 moe_status launch_ffn_f32(const moe_cfg* c, const float* x_perm, const int32_t* perm,
                           const int32_t* offsets, const moe_expert_weights* w, const float* x,
@@ -54,12 +56,13 @@ moe_status launch_gateup_recompute_bf16(const moe_cfg* c, const bf16_t* x_perm, 
                                         const int32_t* ntiles, int64_t max_tiles, bf16_t* g, bf16_t* u,
                                         bf16_t* gs, bf16_t* us, hipStream_t st);
 
-// Backward GEMMs (gemm_bwd.hip): the expert part (recompute g, u; dh -> dgu, h;
-// dx; dW_gu; dW_d) and the router part (dW_r by split-K partials, dx_router).
+// Backward GEMMs (gemm_bwd.hip): the expert part (g, u from saved, or
+// recomputed when saved == nullptr; dh -> dgu, h; dx; dW_gu; dW_d) and the
+// router part (dW_r by split-K partials, dx_router).
 moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf16_t* x, const int32_t* offsets,
-                               const moe_expert_weights* w, const bf16_t* dy_perm, const bf16_t* dy,
-                               bf16_t* dx_perm, bf16_t* dx_shared, const moe_expert_grads* gr, void* ws,
-                               hipStream_t st);
+                               const moe_expert_weights* w, const moe_ffn_saved* saved, const bf16_t* dy_perm,
+                               const bf16_t* dy, bf16_t* dx_perm, bf16_t* dx_shared, const moe_expert_grads* gr,
+                               void* ws, hipStream_t st);
 moe_status launch_router_bwd_gemms(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
                                    const bf16_t* dlogit, float* part, int nsplit, float* dw_router,
                                    float* dx_router, hipStream_t st);

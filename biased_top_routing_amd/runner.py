@@ -5,7 +5,10 @@ need for T tokens, and runs route -> dispatch -> expert FFN -> combine ->
 bias update on the current stream.  It only allocates and marshals; every step
 of the layer runs in libmoe's kernels.  With gather=True, dispatch writes only
 the indices and the routed gate/up GEMM reads its rows from x through perm
-(moe_expert_ffn_gather); no x_perm is allocated.
+(moe_expert_ffn_gather); no x_perm is allocated.  With save_gu=True (bf16),
+the forward pass keeps the gate and up outputs (moe_expert_ffn_save) and the
+backward pass starts from them (moe_expert_ffn_backward_saved) instead of
+recomputing the gate/up GEMM.
 """
 from __future__ import annotations
 
@@ -26,10 +29,11 @@ def to_device(arr, device="cuda"):
 
 
 class MoeLayerGPU:
-    def __init__(self, cfg, weights, T=None, device="cuda", gather=False):
+    def __init__(self, cfg, weights, T=None, device="cuda", gather=False, save_gu=False):
         self.c = cfg
         self.device = device
         self.gather = gather
+        self.save_gu = save_gu
         self.fp8 = cfg.wgt == "fp8_e4m3"
         self.act_dtype = torch.float32 if cfg.act == "f32" else torch.bfloat16
         dev = lambda a: to_device(a, device)
@@ -88,6 +92,13 @@ class MoeLayerGPU:
         self.ws_dispatch = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_DISPATCH), dtype=torch.uint8,
                                        device=d)
         self.ws_ffn = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_FFN), dtype=torch.uint8, device=d)
+        if self.save_gu:
+            bf = torch.bfloat16
+            self.g = torch.empty((P, c.I), dtype=bf, device=d)
+            self.u = torch.empty((P, c.I), dtype=bf, device=d)
+            self.gs = torch.empty((T, c.S * c.I), dtype=bf, device=d) if c.S > 0 else None
+            self.us = torch.empty((T, c.S * c.I), dtype=bf, device=d) if c.S > 0 else None
+            self.saved = L.ffn_saved(self.g, self.u, self.gs, self.us)
 
     # ---------------------------------------------------------------- the five calls
     def route(self, x, bias, scores_in=False):
@@ -99,7 +110,10 @@ class MoeLayerGPU:
                        self.x_perm_scale, self.ws_dispatch)
 
     def expert_ffn(self, x, phase=L.MOE_FFN_ALL):
-        if self.gather:
+        if self.save_gu:
+            L.moe_expert_ffn_save(self.cfg, self.x_perm, self.perm, self.offsets, self.weights, x, self.y_perm,
+                                  self.y_shared, self.saved, self.ws_ffn, phase)
+        elif self.gather:
             L.moe_expert_ffn_gather(self.cfg, x, self.perm, self.offsets, self.weights, self.y_perm,
                                     self.y_shared, self.ws_ffn, phase)
         else:
@@ -145,8 +159,12 @@ class MoeLayerGPU:
             self.alloc_backward()
         cfg = self.cfg
         L.moe_combine_backward(cfg, dy, self.y_perm, self.inv, self.topk_w, self.dy_perm, self.d_topk_w)
-        L.moe_expert_ffn_backward(cfg, self.x_perm, x, self.offsets, self.weights, self.dy_perm, dy, self.dx_perm,
-                                  self.dx_shared, self.grads, self.ws_ffn_bwd)
+        if self.save_gu:
+            L.moe_expert_ffn_backward_saved(cfg, self.x_perm, x, self.offsets, self.weights, self.saved, self.dy_perm,
+                                            dy, self.dx_perm, self.dx_shared, self.grads, self.ws_ffn_bwd)
+        else:
+            L.moe_expert_ffn_backward(cfg, self.x_perm, x, self.offsets, self.weights, self.dy_perm, dy,
+                                      self.dx_perm, self.dx_shared, self.grads, self.ws_ffn_bwd)
         L.moe_route_backward(cfg, x, self.w_router, self.scores, self.topk_idx, self.d_topk_w, alpha, seq_len,
                              self.dx_router, self.g_w_router, self.loss_bal, self.ws_route_bwd)
         L.moe_dispatch_backward(cfg, self.dx_perm, self.dx_shared, self.dx_router, self.inv, self.dx)

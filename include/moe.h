@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -202,6 +202,41 @@ moe_status moe_expert_ffn_gather(const moe_cfg* cfg, const void* x, const int32_
                                  void* y_perm, void* y_shared, void* ws, size_t ws_bytes,
                                  int phase, void* stream);
 
+/* The SwiGLU inputs of the experts (bf16, caller-owned): g = X W_g^T and
+ * u = X W_u^T, [T*k, I] in the expert-sorted row order of x_perm, and the
+ * shared experts' gs, us [T, S*I] (S > 0; expert s in columns [s*I, (s+1)*I)). */
+typedef struct {
+  void* g;
+  void* u;
+  void* gs;
+  void* us;
+} moe_ffn_saved;
+
+/*
+ * moe_expert_ffn_save - moe_expert_ffn (x_perm != NULL) or moe_expert_ffn_gather
+ * (x_perm == NULL: rows gathered from x through perm) that also stores the
+ * gate and up outputs g, u of the gate/up GEMM in `saved`, for a training step
+ * whose backward pass then starts from them (moe_expert_ffn_backward_saved)
+ * instead of recomputing the gate/up GEMM.  Same arithmetic and order: y_perm
+ * and y_shared equal the other entry points' bit for bit, and g, u equal the
+ * backward pass's recomputation bit for bit.  bf16 only (MOE_ERR_UNSUPPORTED
+ * otherwise).  The phase MOE_FFN_DOWN leaves `saved` untouched.
+ *
+ * Follows: the experts are SwiGLU FFNs (DeepSeek-V3 Technical Report：中英对照
+ * 解读, §2); which activations a training step keeps and which it recomputes
+ * is the memory/compute trade-off the pages make for RMSNorm and the MLA
+ * up-projection (qwbw.cn essay, infrastructure section, memory optimisations): keeping g and u costs
+ * 2 * (T*k + T*S) * I * 2 bytes and saves the backward pass one gate/up GEMM.
+ *
+ *  x_perm, perm, offsets, w, x, y_perm, y_shared, ws, ws_bytes, phase  as for
+ *  moe_expert_ffn / moe_expert_ffn_gather; saved: every member non-NULL (gs, us
+ *  when S > 0).
+ */
+moe_status moe_expert_ffn_save(const moe_cfg* cfg, const void* x_perm, const int32_t* perm,
+                               const int32_t* offsets, const moe_expert_weights* w, const void* x,
+                               void* y_perm, void* y_shared, const moe_ffn_saved* saved, void* ws,
+                               size_t ws_bytes, int phase, void* stream);
+
 /*
  * moe_combine - y[t] = y_shared[t] + sum_j topk_w[t, j] * y_perm[inv[t, j]]
  * accumulated in fp32 over j ascending; y in the activation dtype.
@@ -290,6 +325,19 @@ moe_status moe_expert_ffn_backward(const moe_cfg* cfg, const void* x_perm, const
                                    const int32_t* offsets, const moe_expert_weights* w, const void* dy_perm,
                                    const void* dy, void* dx_perm, void* dx_shared, const moe_expert_grads* grads,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_backward_saved - moe_expert_ffn_backward starting from the
+ * gate and up outputs kept by moe_expert_ffn_save (`saved`, every member
+ * non-NULL; gs, us when S > 0) instead of recomputing them: the same outputs,
+ * bit for bit, without the gate/up GEMM.  Arguments otherwise as for
+ * moe_expert_ffn_backward (x_perm is still read, by dW_gu = [dg du]^T X).
+ */
+moe_status moe_expert_ffn_backward_saved(const moe_cfg* cfg, const void* x_perm, const void* x,
+                                         const int32_t* offsets, const moe_expert_weights* w,
+                                         const moe_ffn_saved* saved, const void* dy_perm, const void* dy,
+                                         void* dx_perm, void* dx_shared, const moe_expert_grads* grads, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /*
  * moe_route_backward - gradients through the gates and the router, plus the

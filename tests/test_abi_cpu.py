@@ -21,7 +21,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
     for st in (0, -1, -2, -3, -4, -5):
         assert len(L.status_string(st)) >= 2
 
@@ -146,6 +146,41 @@ def test_backward_validation():
     assert rb(*args(0.1, -4, big)) == L.MOE_ERR_SHAPE
     assert rb(*args(0.1, 1024, need_r - 1)) == L.MOE_ERR_WORKSPACE
     assert rb(ctypes.byref(cfg), 1, 1, 1, 1, 1, 0.0, 0, 1, None, 1, 1, big, None) == L.MOE_ERR_NULL
+
+
+def test_saved_gate_up_validation():
+    """moe_expert_ffn_save / moe_expert_ffn_backward_saved: bf16 only, every saved buffer
+    (the shared ones when S > 0) required, rows from x_perm or perm."""
+    cfg = _cfg()                                              # bf16, S > 0
+    big = 1 << 40
+    lb = L.lib()
+    w = L.MoeExpertWeights(1, 1, None, None, 1, 1, None, None)
+    g = L.MoeExpertGrads(1, 1, 1, 1)
+    full, no_shared = L.MoeFfnSaved(1, 1, 1, 1), L.MoeFfnSaved(1, 1, None, None)
+    fs = lb.moe_expert_ffn_save
+    assert fs(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, None, 1, big, 0, None) == L.MOE_ERR_NULL
+    assert fs(ctypes.byref(cfg), None, None, 1, ctypes.byref(w), 1, 1, 1, ctypes.byref(full), 1, big, 0, None) \
+        == L.MOE_ERR_NULL                                     # neither x_perm nor perm
+    assert fs(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, ctypes.byref(no_shared), 1, big, 0,
+              None) == L.MOE_ERR_NULL                         # S > 0 needs gs, us
+    for bad in (L.cfg_from(V3_FP8), L.cfg_from(TINY)):
+        assert fs(ctypes.byref(bad), 1, None, 1, ctypes.byref(w), 1, 1, 1, ctypes.byref(full), 1, big, 0,
+                  None) != L.MOE_OK
+    assert fs(ctypes.byref(L.cfg_from(TINY)), 1, None, 1, ctypes.byref(w), 1, 1, 1, ctypes.byref(full), 1, big,
+              0, None) == L.MOE_ERR_UNSUPPORTED              # fp32 layer
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN)
+    assert fs(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, ctypes.byref(full), 1, need - 1, 0, None) \
+        == L.MOE_ERR_WORKSPACE
+    bs = lb.moe_expert_ffn_backward_saved
+    need_b = L.moe_workspace_bytes(cfg, L.MOE_WS_FFN_BWD)
+    assert bs(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), None, 1, 1, 1, 1, ctypes.byref(g), 1, big, None) \
+        == L.MOE_ERR_NULL
+    assert bs(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), ctypes.byref(no_shared), 1, 1, 1, 1, ctypes.byref(g), 1,
+              big, None) == L.MOE_ERR_NULL
+    assert bs(ctypes.byref(cfg), 1, 1, 1, ctypes.byref(w), ctypes.byref(full), 1, 1, 1, 1, ctypes.byref(g), 1,
+              need_b - 1, None) == L.MOE_ERR_WORKSPACE
+    assert bs(ctypes.byref(L.cfg_from(V3_FP8)), 1, 1, 1, ctypes.byref(w), ctypes.byref(full), 1, 1, 1, 1,
+              ctypes.byref(g), 1, big, None) == L.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes_scale_with_tokens():

@@ -104,3 +104,32 @@ def test_backward_matches_oracle(name):
         assert abs(loss - o["loss_bal"]) <= 1e-4 * abs(o["loss_bal"]), (loss, o["loss_bal"])
     else:
         assert loss == 0.0
+
+
+@pytest.mark.parametrize("name", ["s2_ragged_tiles", "zipf_no_shared_no_loss"])
+def test_saved_gate_up_matches_recompute(name):
+    """A forward pass that keeps g, u (moe_expert_ffn_save) gives the same y as one that
+    does not, and the backward pass from the kept g, u (moe_expert_ffn_backward_saved)
+    the same gradients as the one that recomputes them, bit for bit (the same GEMM
+    computes both, in the same order)."""
+    c, alpha, seq_len = CASES[name]
+    w = make_weights(c)
+    xh = make_x(c)
+    dyh = f32_to_bf16_bits(rng(98, c.T).normal(size=(c.T, c.H)).astype(np.float32))
+    say(f"saved g/u {name}")
+    layer = MoeLayerGPU(c, w, save_gu=True)
+    x, dy = to_device(xh), to_device(dyh)
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    y_saved = _bits(layer.forward(x, bias)).copy()
+    layer.backward(x, dy, alpha, seq_len)
+    torch.cuda.synchronize()
+    keys = ["dx", "dx_shared", "dx_perm", "g_w_gate_up", "g_w_down", "g_ws_gate_up", "g_ws_down", "g_w_router",
+            "loss_bal"]
+    saved = {k: _bits(getattr(layer, k)).copy() for k in keys if getattr(layer, k) is not None}
+    layer.save_gu = False                      # same buffers, the recomputing entry points
+    y_plain = _bits(layer.forward(x, bias)).copy()
+    layer.backward(x, dy, alpha, seq_len)
+    torch.cuda.synchronize()
+    assert (y_saved == y_plain).all(), "y differs with and without keeping g, u"
+    for k, v in saved.items():
+        assert (v == _bits(getattr(layer, k))).all(), f"{k}: saved g, u and recomputation differ"
