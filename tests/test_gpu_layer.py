@@ -241,3 +241,42 @@ def test_router_gemm_tile_heights(T, E):
     assert np.abs(s_gpu - s_ora).max() < 1e-5
     idx_o, _ = oracle.route(s_gpu, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale)
     assert (host(idx) == idx_o).all()
+
+
+# ---------------------------------------------------------------- gate/up row tiling boundaries
+SEG_SIZES = [1, 96, 128, 129, 160, 161, 192, 256, 257, 320, 321, 384, 512, 513, 576, 640, 641, 700, 768, 769]
+
+
+def test_expert_segments_at_row_tile_boundaries():
+    """Expert segments at every boundary of the row tiling (gate/up: 320-row tiles, or 256-row
+    tiles where that takes no more of them, wavefront bands of 160 / 128 rows; down: 256-row
+    tiles, 64-row bands), routed from given scores (top-1 of 20 experts, one group): every
+    segment's y_perm against the fp64 oracle, and the gather and keep-g,u entry points bit
+    for bit against the row-copy one."""
+    E, T = len(SEG_SIZES), sum(SEG_SIZES)
+    c = MID.with_(T=T, H=256, E=E, G=1, M=1, k=1, S=1, I=256, group_topr=1, sigma=0.05)
+    w = make_weights(c)
+    xb = make_x(c)
+    target = rng(7, 1).permutation(np.repeat(np.arange(E), SEG_SIZES))
+    s32 = np.full((T, E), 0.25, np.float32)
+    s32[np.arange(T), target] = 0.75
+    say(f"segments at tile boundaries: T={T}, E={E}")
+    outs = {}
+    for mode in ("copy", "gather", "save"):
+        layer = MoeLayerGPU(c, w, gather=mode == "gather", save_gu=mode == "save")
+        layer.scores.copy_(dev_f32(s32))
+        layer.forward(to_device(xb), dev_f32(w.bias0), scores_in=True)
+        torch.cuda.synchronize()
+        outs[mode] = (host(layer.y_perm), host(layer.y), host(layer.offsets))
+    ref = oracle.forward_from_routing(c, xb, w, w.bias0, s32, *oracle.route(
+        s32, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale))
+    yp, y, offs = outs["copy"]
+    assert (offs == np.concatenate([[0], np.cumsum(SEG_SIZES)])).all()
+    for e in range(E):
+        lo, hi = offs[e], offs[e + 1]
+        err = rel_inf(yp[lo:hi], ref["y_perm"][lo:hi])
+        assert err < 2e-2, (e, SEG_SIZES[e], err)
+    assert rel_inf(y, ref["y"]) < 2e-2
+    for mode in ("gather", "save"):
+        assert (outs[mode][0].view(np.uint32) == yp.view(np.uint32)).all(), f"{mode}: y_perm bits differ"
+        assert (outs[mode][1].view(np.uint32) == y.view(np.uint32)).all(), f"{mode}: y bits differ"
