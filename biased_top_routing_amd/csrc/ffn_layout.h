@@ -33,8 +33,9 @@ inline size_t dispatch_ws_bytes(const moe_cfg* c) {
 #ifndef MOE_DN_TILE
 #define MOE_DN_TILE 4, 4, 2, 2, 64, 2, 1
 #endif
-// Router GEMM tiles (tokens x experts): 64, 128 or 256 tokens x 256 experts,
-// 8 wavefronts; the launcher picks the tallest that still fills the GPU
+// Router GEMM tiles (tokens x experts): 64 x 256, 128 x 256, 128 x 128 and
+// 256 x 256, 8 wavefronts; the launcher picks the largest whose grid still
+// covers every CU (small batches use the split-K router kernel instead)
 #ifndef MOE_RT_TILE
 #define MOE_RT_TILE 2, 4, 1, 2, 64, 3, 1
 #endif
