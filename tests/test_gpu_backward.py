@@ -133,3 +133,32 @@ def test_saved_gate_up_matches_recompute(name):
     assert (y_saved == y_plain).all(), "y differs with and without keeping g, u"
     for k, v in saved.items():
         assert (v == _bits(getattr(layer, k))).all(), f"{k}: saved g, u and recomputation differ"
+
+
+def test_save_by_phase():
+    """moe_expert_ffn_save run as its two phases (gate/up, then down) writes the same g, u,
+    y_perm and y_shared as one call, and the down phase leaves the kept g, u untouched."""
+    from biased_top_routing_amd import _lib as L
+    c, _, _ = CASES["s2_ragged_tiles"]
+    w = make_weights(c)
+    xh = make_x(c)
+    layer = MoeLayerGPU(c, w, save_gu=True)
+    x = to_device(xh)
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    layer.forward(x, bias)
+    torch.cuda.synchronize()
+    whole = {k: _bits(getattr(layer, k)).copy() for k in ("g", "u", "gs", "us", "y_perm", "y_shared")}
+    for k in ("g", "u", "gs", "us", "y_perm", "y_shared"):
+        getattr(layer, k).zero_()
+    layer.expert_ffn(x, L.MOE_FFN_GATE_UP)
+    torch.cuda.synchronize()
+    kept = {k: _bits(getattr(layer, k)).copy() for k in ("g", "u", "gs", "us")}
+    for k in ("g", "u", "gs", "us"):
+        getattr(layer, k).fill_(1.0)                  # the down phase must not touch them
+    layer.expert_ffn(x, L.MOE_FFN_DOWN)
+    torch.cuda.synchronize()
+    for k in ("g", "u", "gs", "us"):
+        assert (kept[k] == whole[k]).all(), f"{k} from the gate/up phase differs"
+        assert (getattr(layer, k) == 1.0).all(), f"the down phase wrote {k}"
+    for k in ("y_perm", "y_shared"):
+        assert (_bits(getattr(layer, k)) == whole[k]).all(), f"{k} by phases differs"
