@@ -209,3 +209,32 @@ def test_v3_prefill_backward_full_size(v3):
         e2 = rel_inf(host(layer.g_w_down[e]), dwd)
         say(f"    dW_gate_up err {e1:.2e}, dW_down err {e2:.2e}")
         assert e1 < 2e-2 and e2 < 2e-2
+
+
+def test_v3_prefill_saved_backward_bit_exact(v3):
+    """At the full V3-like size, the training step that keeps g, u in the forward pass
+    (moe_expert_ffn_save + moe_expert_ffn_backward_saved) gives the same forward output
+    and the same gradients, bit for bit, as the one that recomputes them."""
+    w, layer = v3
+    c = V3_PREFILL
+    layer.save_gu = True
+    layer.alloc(c.T)                                  # buffers for g, u
+    xh = make_x(c, 0)
+    x = to_device(xh)
+    dy = to_device(f32_to_bf16_bits(rng(33, c.T).normal(size=(c.T, c.H)).astype(np.float32)))
+    bias = dev_f32(w.bias0)
+    keys = ["dx", "dx_shared", "g_w_gate_up", "g_w_down", "g_ws_gate_up", "g_ws_down", "g_w_router", "loss_bal"]
+    iview = lambda t: t.view(torch.int32 if t.dtype == torch.float32 else torch.int16)
+    kept = None
+    for save in (True, False):
+        layer.save_gu = save
+        say(f"v3: forward + backward, g and u {'kept' if save else 'recomputed'}")
+        y = layer.forward(x, bias)
+        layer.backward(x, dy, 1e-3, 4096)
+        torch.cuda.synchronize()
+        if save:                                      # one copy (the weight gradients are 45 GB of fp32)
+            kept = {"y": y.clone(), **{k: getattr(layer, k).clone() for k in keys}}
+    layer.save_gu = False
+    assert torch.equal(iview(kept["y"]), iview(y)), "y differs"
+    for k in keys:
+        assert torch.equal(iview(kept[k]), iview(getattr(layer, k))), f"{k} differs"
