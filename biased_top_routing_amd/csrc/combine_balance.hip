@@ -56,6 +56,8 @@ __device__ __forceinline__ void accum_chunk(float* acc, uint4 r, float g) {
   }
 }
 
+constexpr int kMaxCombineK = 32;   // validate_cfg bounds k
+
 template <bool BF16>
 __global__ __launch_bounds__(1024) void combine_kernel(const uint4* __restrict__ y_perm,
                                                       const uint4* __restrict__ y_shared,
@@ -64,12 +66,20 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint4* __restrict__
                                                       int k, int64_t nchunk,
                                                       uint4* __restrict__ y) {
   constexpr int KB = 8;   // routed rows loaded per batch
-  const int lane = threadIdx.x & 63;
+  // The token's slot rows and gates, read once into LDS while every lane is
+  // active: the chunk loop below is divergent in its last wavefront (nchunk
+  // need not be a multiple of 64), so the slot values must not come from
+  // cross-lane moves inside it (a lane that left the loop supplies nothing).
+  __shared__ int32_t slot_row[kMaxCombineK];
+  __shared__ float slot_w[kMaxCombineK];
   const int64_t t = blockIdx.x;          // the whole workgroup on one token
   const int c0 = threadIdx.x, cstep = blockDim.x;
   if (t >= T) return;
-  const int32_t myp = lane < k ? inv[t * k + lane] : 0;
-  const float myw = lane < k ? topk_w[t * k + lane] : 0.f;
+  if ((int)threadIdx.x < k) {
+    slot_row[threadIdx.x] = inv[t * k + threadIdx.x];
+    slot_w[threadIdx.x] = topk_w[t * k + threadIdx.x];
+  }
+  __syncthreads();
   constexpr int V = BF16 ? 8 : 4;
   for (int64_t c = c0; c < nchunk; c += cstep) {
     float acc[V];
@@ -82,14 +92,12 @@ __global__ __launch_bounds__(1024) void combine_kernel(const uint4* __restrict__
       for (int jj = 0; jj < KB; ++jj) {
         // slots past k reload slot j0's row (kept in range, weight 0 below)
         const int j = j0 + jj < k ? j0 + jj : j0;
-        const int64_t p = __shfl(myp, j);
+        const int64_t p = slot_row[j];
         r[jj] = ld_stream(&y_perm[p * nchunk + c]);
       }
 #pragma unroll
       for (int jj = 0; jj < KB; ++jj) {
-        const int j = j0 + jj < k ? j0 + jj : j0;
-        const float g = __shfl(myw, j);
-        if (j0 + jj < k) accum_chunk<BF16>(acc, r[jj], g);
+        if (j0 + jj < k) accum_chunk<BF16>(acc, r[jj], slot_w[j0 + jj]);
       }
     }
     uint4 o;

@@ -58,6 +58,47 @@ def test_combine(act):
     assert rel_inf(host(y), ref) < tol
 
 
+# Rows whose 16-byte chunk count leaves a last wavefront with fewer active lanes than k
+# (0 < nchunk mod 64 < k), and a second pass over the row (nchunk > 1024): every slot
+# of every chunk must still be added.
+COMBINE_TAIL_CASES = [
+    # (act, T, H, E, G, M, k)
+    ("bf16", 37, 576, 32, 4, 2, 16),     # 72 chunks: 8 lanes in the last wavefront
+    ("bf16", 9, 8256, 32, 4, 2, 16),     # 1032 chunks: a second pass of 8 lanes
+    ("f32", 41, 68, 32, 4, 4, 24),       # 17 chunks
+    ("f32", 50, 12, 8, 2, 2, 4),         # 3 chunks
+]
+
+
+@pytest.mark.parametrize("act,T,H,E,G,M,k", COMBINE_TAIL_CASES)
+def test_combine_ragged_row_tail(act, T, H, E, G, M, k):
+    say(f"combine tail {act} T={T} H={H} k={k}")
+    cfg = L.make_cfg(T, H, E, G, M, k, 1, 128 if act == "bf16" else 4, 2, 1.0, act, act)
+    g = rng(12, H, k)
+    idx = np.argsort(-g.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    _, _, perm, inv = oracle.dispatch(idx, E)
+    w = (g.random((T, k)) + 0.5).astype(np.float32)
+    yp = g.standard_normal((T * k, H)).astype(np.float32)
+    ys = g.standard_normal((T, H)).astype(np.float32)
+    if act == "bf16":
+        yp_d, ys_d = _bf16_dev(yp), _bf16_dev(ys)
+        yp_v, ys_v = _dec(f32_to_bf16_bits(yp)), _dec(f32_to_bf16_bits(ys))
+        y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+        tol = 2 ** -8
+    else:
+        yp_d, ys_d, yp_v, ys_v = dev_f32(yp), dev_f32(ys), yp, ys
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        tol = 1e-6
+    L.moe_combine(cfg, yp_d, ys_d, dev_i32(inv), dev_f32(w), y)
+    torch.cuda.synchronize()
+    ref = oracle.combine(yp_v, ys_v, inv, w)
+    got = host(y)
+    # elementwise as well: a dropped slot changes single elements by a whole term
+    scale = np.abs(ref).max()
+    assert np.abs(got - ref).max() < tol * scale
+    assert rel_inf(got, ref) < tol
+
+
 # ---------------------------------------------------------------- expert GEMMs on given routing
 FFN_CASES = [
     # (T, H, E, G, M, k, S, I) -- several tiles, ragged row tails, shared experts
@@ -66,6 +107,7 @@ FFN_CASES = [
     (64, 512, 4, 4, 4, 4, 0, 384),
     (1, 256, 8, 2, 1, 2, 1, 128),
     (1000, 1024, 64, 8, 3, 6, 2, 256),
+    (300, 576, 32, 4, 2, 16, 1, 128),   # combine rows of 72 chunks with k = 16 slots
 ]
 
 
@@ -215,32 +257,51 @@ def test_layer_determinism_and_routing_invariants():
     np.testing.assert_allclose(w, c.route_scale * sel / sel.sum(1, keepdims=True), rtol=2e-6, atol=0)
 
 
-@pytest.mark.parametrize("T,E", [(1, 256), (128, 256), (300, 200), (1000, 256), (8192, 256), (16384, 256), (16384, 192),
-                                 (32768, 64), (65613, 64)])
+@pytest.mark.parametrize("T,E", [(1, 256), (128, 256), (300, 200), (1000, 256), (2048, 256), (2049, 256),
+                                 (8192, 256), (16384, 256), (16384, 192), (12345, 64), (16384, 64), (32768, 64),
+                                 (65613, 64)])
 def test_router_gemm_tile_heights(T, E):
-    """The router GEMM's kernel and tile follow the batch on a 256-CU chip: the
-    split-K kernel with 16 x 16 tiles (T = 1, 128; T = 300 with ragged token and
-    expert tiles) and 32 x 32 tiles (T = 1000), then 64 x 256 (T = 8192), 128 x 128
-    (T = 16384 with two column tiles of experts, the second ragged for E = 192),
-    128 x 256 and 256 x 256 (the last with a ragged final row tile): affinities
-    against the fp64 oracle, routing teacher-forced bit for bit."""
+    """The router's kernel and tile follow the batch on a 256-CU chip: the split-K kernel
+    with 16 x 16 tiles (T = 1, 128; T = 300 with ragged token and expert tiles) and
+    32 x 32 tiles (T = 1000, 2048); then, while no larger tile fills the chip, the fused
+    kernel (router GEMM with the top-k in its epilogue) with 64-token tiles of all experts
+    (E = 256: T = 2049 with one token in the last tile, 8192; E = 64: T = 12345, 16384);
+    then the two-kernel path with 128 x 128 tiles (T = 16384, E = 256, and E = 192 with
+    a ragged second column tile), 128 x 256 (T = 32768, E = 64) and 256 x 256 (T = 65613,
+    ragged last row tile).  Affinities against the fp64 oracle, routing teacher-forced bit
+    for bit; the same call without the affinities and the top-k alone on the written
+    affinities give the same indices and gates bit for bit."""
     from biased_top_routing_amd import _lib as L
     c = MID.with_(T=T, H=256, E=E, I=128, S=1)
     w = make_weights(c)
     xh = make_x(c)
-    say(f"router T={T}")
+    say(f"router T={T} E={E}")
     cfg = L.cfg_from(c)
+    x, wr, off, b = to_device(xh), to_device(w.w_router), to_device(w.logit_offset), dev_f32(w.bias0)
     s = torch.empty((T, c.E), dtype=torch.float32, device="cuda")
-    idx = torch.empty((T, c.k), dtype=torch.int32, device="cuda")
-    wt = torch.empty((T, c.k), dtype=torch.float32, device="cuda")
-    L.moe_route(cfg, to_device(xh), to_device(w.w_router), to_device(w.logit_offset), dev_f32(w.bias0), s, 0, idx, wt)
-    torch.cuda.synchronize()
+    outs = []
+    for mode in ("scores", "no scores", "scores in"):
+        idx = torch.full((T, c.k), -1, dtype=torch.int32, device="cuda")
+        wt = torch.full((T, c.k), -1.0, dtype=torch.float32, device="cuda")
+        if mode == "scores":
+            L.moe_route(cfg, x, wr, off, b, s, 0, idx, wt)
+        elif mode == "no scores":
+            ws = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE), dtype=torch.uint8, device="cuda")
+            L.moe_route(cfg, x, wr, off, b, None, 0, idx, wt, ws)
+        else:
+            L.moe_route(cfg, None, None, None, b, s, L.MOE_SCORES_IN, idx, wt)
+        torch.cuda.synchronize()
+        outs.append((host(idx), host(wt)))
     s_gpu = host(s)
     s_ora = oracle.affinity(oracle.decode_act(xh).astype(np.float64), oracle.decode_act(w.w_router).astype(np.float64),
                             w.logit_offset)
     assert np.abs(s_gpu - s_ora).max() < 1e-5
-    idx_o, _ = oracle.route(s_gpu, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale)
-    assert (host(idx) == idx_o).all()
+    idx_o, w_o = oracle.route(s_gpu, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale)
+    assert (outs[0][0] == idx_o).all()
+    np.testing.assert_allclose(outs[0][1], w_o, rtol=2e-6, atol=1e-7)
+    for idx_m, w_m in outs[1:]:
+        assert (idx_m == outs[0][0]).all()
+        assert (w_m.view(np.uint32) == outs[0][1].view(np.uint32)).all()
 
 
 # ---------------------------------------------------------------- gate/up row tiling boundaries
@@ -280,3 +341,33 @@ def test_expert_segments_at_row_tile_boundaries():
     for mode in ("gather", "save"):
         assert (outs[mode][0].view(np.uint32) == yp.view(np.uint32)).all(), f"{mode}: y_perm bits differ"
         assert (outs[mode][1].view(np.uint32) == y.view(np.uint32)).all(), f"{mode}: y bits differ"
+
+
+def test_layer_resume_from_saved_bias(tmp_path):
+    """The bias is the layer's only state across batches.  Ten batches in one run equal
+    five batches, the bias written to a file and read back into a freshly built layer,
+    then five more batches: the layer outputs of batches 5..9 and the final bias are
+    identical bit for bit (tiny fp32 workload, fresh x per batch)."""
+    c = TINY
+    wts = make_weights(c)
+    xs = [make_x(c, step) for step in range(10)]
+
+    def run(layer, bias, steps):
+        ys = []
+        for step in steps:
+            say(f"resume test batch {step}")
+            ys.append(host(layer.forward(to_device(xs[step]), bias, gamma=c.gamma)).copy())
+        torch.cuda.synchronize()
+        return ys
+
+    bias_a = dev_f32(wts.bias0)
+    ys_a = run(MoeLayerGPU(c, wts), bias_a, range(10))
+    bias_b = dev_f32(wts.bias0)
+    run(MoeLayerGPU(c, wts), bias_b, range(5))
+    path = tmp_path / "bias.npy"
+    np.save(path, host(bias_b))
+    bias_c = dev_f32(np.load(path))
+    ys_c = run(MoeLayerGPU(c, wts), bias_c, range(5, 10))
+    for a, b in zip(ys_a[5:], ys_c):
+        assert (a.view(np.uint32) == b.view(np.uint32)).all()
+    assert (host(bias_a).view(np.uint32) == host(bias_c).view(np.uint32)).all()
