@@ -91,10 +91,14 @@ def quantize_blocks_128x128(w) -> tuple:
     return q.reshape(N, K), sc
 
 
+# value of every byte, for decoding large arrays by lookup (the same values e4m3_decode gives)
+_DECODE = e4m3_decode(np.arange(256, dtype=np.uint8))
+
+
 def fp8_matmul(qa, sa, qw, sw) -> np.ndarray:
     """out[r, n] = sum_c (sum_{k in chunk c} a_code*w_code) * sa[r, c] * sw[n // 128, c]  (fp64)."""
-    A = e4m3_decode(qa)
-    W = e4m3_decode(qw)
+    A = _DECODE[np.asarray(qa, np.uint8)]
+    W = _DECODE[np.asarray(qw, np.uint8)]
     R, K = A.shape
     N = W.shape[0]
     out = np.zeros((R, N), F64)

@@ -126,18 +126,27 @@ def forward_from_routing(cfg, x, weights, bias, s32, idx, w):
 def sampled_forward(cfg, x_rows, idx_rows, w_rows, weights, experts_cache=None):
     """Layer output for a subset of tokens, given their routing (tokens are
     independent once routed).  x_rows [n, H] stored values; idx_rows, w_rows [n, k].
-    Returns y_rows [n, H] fp64 (shared + gated routed outputs)."""
+    Returns y_rows [n, H] fp64 (shared + gated routed outputs).
+    experts_cache: optional dict that keeps each expert's prepared form (keys e for
+    routed experts, ("shared", s) for shared ones) between calls."""
     x32 = decode_act(x_rows)
     view = _rows_view(cfg, x32)
     n = x32.shape[0]
     y = np.zeros((n, cfg.H), F64)
+    cache = {} if experts_cache is None else experts_cache
+
+    def expert(key, w_gate_up, w_down):
+        if key not in cache:
+            cache[key] = _expert_fn(cfg, w_gate_up, w_down)
+        return cache[key]
+
     for s in range(cfg.S):
-        y += _expert_fn(cfg, weights.ws_gate_up[s], weights.ws_down[s])(view)
+        y += expert(("shared", s), weights.ws_gate_up[s], weights.ws_down[s])(view)
     idx_rows = np.asarray(idx_rows)
     w_rows = np.asarray(w_rows, F64)
     for e in np.unique(idx_rows):
         r, j = np.nonzero(idx_rows == e)
-        f = _expert_fn(cfg, weights.w_gate_up[e], weights.w_down[e])
+        f = expert(int(e), weights.w_gate_up[e], weights.w_down[e])
         ye = f(_take(view, r))
         y[r] += w_rows[r, j][:, None] * ye
     return y

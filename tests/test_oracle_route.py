@@ -195,6 +195,45 @@ def _check_ties(qrow, idxrow, G, M, k):
     assert idxrow.tolist() == exp
 
 
+def test_diagnostics_worked_example():
+    """Hand-derived margins of the worked example (k-th minus (k+1)-th biased score among
+    the allowed experts; M-th minus (M+1)-th group score)."""
+    g = _load("route_worked_example.json")
+    s = np.array(g["scores"], np.float32)
+    b = np.array(g["bias"], np.float32)
+    gk, gm = oracle.route_diagnostics(s, b, g["G"], g["M"], g["k"], 2)
+    assert gk.tolist() == g["r2_gaps"]["gap_k"]
+    assert gm.tolist() == g["r2_gaps"]["gap_m"]
+    gk1, gm1 = oracle.route_diagnostics(s, b, g["G"], g["M"], g["k"], 1)
+    assert (gk1[0], gm1[0]) == (g["r1_token0_gaps"]["gap_k"], g["r1_token0_gaps"]["gap_m"])
+    gk0, gm0 = oracle.route_diagnostics(s, np.zeros(8, np.float32), g["G"], g["M"], g["k"], 2)
+    assert (gk0[0], gm0[0]) == (g["no_bias_token0_gaps"]["gap_k"], g["no_bias_token0_gaps"]["gap_m"])
+
+
+@pytest.mark.parametrize("E,G,M,k,r", [(16, 4, 2, 4, 2), (12, 3, 2, 5, 3), (16, 8, 3, 4, 1)])
+def test_diagnostics_brute_force(E, G, M, k, r):
+    """The margins from enumeration: gap_m = the smallest group score among the best M-subset
+    of groups minus the largest outside it; gap_k = the smallest biased score of the best
+    k-subset of the allowed experts minus the largest allowed score outside it."""
+    T = 30
+    s, b = _dyadic_tie_free(E * 100 + G * 10 + M + 7, T, E, G, r)
+    gk, gm = oracle.route_diagnostics(s, b, G, M, k, r)
+    q = (s + b).astype(np.float64)
+    gsz = E // G
+    for t in range(T):
+        row = list(q[t])
+        gscore = [max(sum(c) for c in itertools.combinations(row[x * gsz:(x + 1) * gsz], r)) for x in range(G)]
+        best_g = max(itertools.combinations(range(G), M), key=lambda gs: sum(gscore[x] for x in gs))
+        rest_g = [x for x in range(G) if x not in best_g]
+        exp_m = min(gscore[x] for x in best_g) - max(gscore[x] for x in rest_g) if rest_g else np.inf
+        allowed = [e for e in range(E) if e // gsz in best_g]
+        best = max(itertools.combinations(allowed, k), key=lambda es: sum(row[e] for e in es))
+        rest = [e for e in allowed if e not in best]
+        exp_k = min(row[e] for e in best) - max(row[e] for e in rest) if rest else np.inf
+        assert gm[t] == pytest.approx(exp_m, rel=0, abs=1e-12)
+        assert gk[t] == pytest.approx(exp_k, rel=0, abs=1e-12)
+
+
 def test_diagnostics_gaps():
     E, G, M, k = 16, 4, 2, 4
     s = make_scores(10, 100, E, kind="ties")
