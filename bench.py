@@ -56,12 +56,15 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes(c, gather=False):
+def stage_bytes(c, gather=False, scores=False):
     """Algorithmic HBM bytes of the bandwidth-bound stages (per layer pass).  With
-    gather, dispatch moves indices only (the rows are read by the gate/up GEMM)."""
+    gather, dispatch moves indices only (the rows are read by the gate/up GEMM).
+    Without scores the route stage reads x, W_r and the bias and writes idx and w
+    (the [T, E] affinities stay on chip); with them it also writes and reads them."""
     a = 2  # bf16
-    route = c.T * c.E * 4 + c.E * 4 + c.T * c.k * 8                      # scores in, bias, idx + w out
-    router = c.T * c.H * a + c.E * c.H * a + c.T * c.E * 4                # x + W_r in, scores out
+    sc = c.T * c.E * 4 if scores else 0
+    route = sc + c.E * 4 + c.T * c.k * 8                                   # (scores in), bias, idx + w out
+    router = c.T * c.H * a + c.E * c.H * a + sc                           # x + W_r in, (scores out)
     dispatch = c.T * c.k * 4 * 4                                          # idx in (twice), perm + inv out
     if not gather:
         dispatch += c.T * c.H * a + c.T * c.k * c.H * a                   # x in, x_perm out
@@ -309,29 +312,45 @@ def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
 
 
 def balance_trajectory(layer, c, w, steps):
-    """Max/mean expert load over `steps` consecutive batches of the layer with the bias
-    update between them.  Each batch's x is drawn on the GPU (torch's generator seeded
-    with the step number, N(0,1), rounded to bf16): same distribution as the shared
-    generator, without minutes of host-side sampling."""
+    """Per-step expert load over `steps` consecutive batches of the layer with the bias
+    update between them.  Batch i's x is make_x(c, i) from the shared seeded generator
+    (the oracle can replay every step); per step the max/mean, min/mean and the
+    coefficient of variation (std/mean) of the per-expert loads."""
+    import numpy as np
     import torch
+
+    from workloads.inputs import make_x
     bias = torch.from_numpy(w.bias0.copy()).cuda()
-    g = torch.Generator(device="cuda")
-    ratios = []
     mean = c.T * c.k / c.E
+    mx, mn, cv = [], [], []
+    t0 = time.perf_counter()
     for step in range(steps):
-        g.manual_seed(1000 + step)
-        x = torch.randn(c.T, c.H, device="cuda", generator=g).to(torch.bfloat16)
+        x = to_dev(make_x(c, step))
         layer.forward(x, bias, gamma=c.gamma)
-        ratios.append(float(layer.counts.max().item()) / mean)
-    pick = [1, 10, 25, 50, 100]
-    return {"steps": steps, "max_over_mean_at_step": {str(i): round(ratios[i - 1], 3) for i in pick if i <= steps},
-            "min_over_steps": round(min(ratios), 3), "x": "N(0,1) drawn on the GPU per step, seeded"}
+        counts = layer.counts.cpu().numpy().astype(np.float64)
+        mx.append(round(float(counts.max() / mean), 4))
+        mn.append(round(float(counts.min() / mean), 4))
+        cv.append(round(float(counts.std() / mean), 4))
+        if step % 20 == 19:
+            log(f"  balance step {step + 1}/{steps} ({time.perf_counter() - t0:.0f} s)")
+    hot = int(np.argmax(counts))
+    b_end = bias.cpu().numpy()
+    return {"steps": steps, "gamma": c.gamma, "x": "make_x(cfg, step): N(0,1) from the shared seeded generator",
+            "max_over_mean": mx, "min_over_mean": mn, "cv": cv,
+            "hottest_expert": hot, "hottest_expert_bias_start": float(w.bias0[hot]),
+            "hottest_expert_bias_end": float(b_end[hot]),
+            "note": ("with Zipf(1.5) logit offsets the hottest experts' offsets (up to +4.6) dwarf what "
+                     "100 steps of gamma = 1e-3 can move (0.1), so every token keeps choosing them and "
+                     "max/mean stays at T / (T k / E) = E / k = 32; the bias of each such expert falls by "
+                     "gamma every step")}
 
 
 def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
-    """The route stage alone (router GEMM + sigmoid + biased group-limited top-k) and the
-    top-k kernel alone (scores given) at several batch sizes, with a 512 MB write
-    between launches so that no input is served from the 256 MB Infinity Cache."""
+    """The route stage (router GEMM + sigmoid + biased group-limited top-k + gates) at
+    several batch sizes, with a 512 MB write between launches so that no input is served
+    from the 256 MB Infinity Cache: "route" without the [T, E] affinities (the forward
+    pass; the fused kernel keeps them on chip), "route_scores" writing them (a training
+    step's forward pass), and "topk" the selection alone on given affinities."""
     import torch
 
     from biased_top_routing_amd import _lib as L
@@ -344,25 +363,30 @@ def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
         cfg = L.cfg_from(c, T=T)
         x = torch.randn(T, c.H, device="cuda").to(torch.bfloat16)
         scores = torch.empty(T, c.E, device="cuda")
+        ws = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE), dtype=torch.uint8, device="cuda")
         idx = torch.empty(T, c.k, dtype=torch.int32, device="cuda")
         gw = torch.empty(T, c.k, device="cuda")
         res = {}
-        for name, flags in (("route", 0), ("topk", L.MOE_SCORES_IN)):
-            L.moe_route(cfg, x, wr, off, bias, scores, flags, idx, gw)
+        xw = T * c.H * 2 + c.E * c.H * 2
+        sc = T * c.E * 4
+        for name, flags, s_arg, nbytes in (("route", 0, None, xw),
+                                           ("route_scores", 0, scores, xw + sc),
+                                           ("topk", L.MOE_SCORES_IN, scores, sc)):
+            nbytes += c.E * 4 + T * c.k * 8
+            L.moe_route(cfg, x, wr, off, bias, s_arg, flags, idx, gw, ws)
             ms = []
             for _ in range(iters):
                 flush.fill_(1)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                L.moe_route(cfg, x, wr, off, bias, scores, flags, idx, gw)
+                L.moe_route(cfg, x, wr, off, bias, s_arg, flags, idx, gw, ws)
                 e1.record()
                 torch.cuda.synchronize()
                 ms.append(e0.elapsed_time(e1))
             t = sorted(ms)[len(ms) // 2]
-            nbytes = (T * c.H * 2 + c.E * c.H * 2 + T * c.E * 4 if flags == 0 else T * c.E * 4) + c.E * 4 + T * c.k * 8
             res[name] = {"ms": round(t, 4), "gbs": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes}
         out[str(T)] = res
-        del x, scores, idx, gw
+        del x, scores, idx, gw, ws
     del flush
     torch.cuda.empty_cache()
     return out
@@ -378,7 +402,7 @@ def small_workload(name, steps, warmup, balance_steps, gather=False):
     from workloads.inputs import make_weights, make_x
     c = CONFIGS[name]
     w = make_weights(c)
-    layer = MoeLayerGPU(c, w, gather=gather)
+    layer = MoeLayerGPU(c, w, gather=gather, keep_scores=False)
     x = to_dev(make_x(c, 0))
     bias = torch.from_numpy(w.bias0.copy()).cuda()
     ms, stage_ms = time_layer(layer, x, bias, c, steps, warmup)
@@ -440,7 +464,7 @@ def main():
         print(json.dumps(train_extra(c, w, args.steps, args.warmup)), flush=True)
         return
     gather = args.dispatch == "gather"
-    layer = MoeLayerGPU(c, w, gather=gather)
+    layer = MoeLayerGPU(c, w, gather=gather, keep_scores=False)
     x = to_dev(xh)
     bias = torch.from_numpy(w.bias0.copy()).cuda()
     torch.cuda.synchronize()
@@ -461,7 +485,7 @@ def main():
 
     peak, gu_tflops, dn_tflops = gemm_summary(c, ms_per_step, stage_ms)
     total_flops = c.gate_up_flops() + c.down_flops() + c.router_flops()
-    b = stage_bytes(c, gather)
+    b = stage_bytes(c, gather, scores=layer.keep_scores)
     route_gbs = (b["router"] + b["topk"]) / (stage_ms["route"] * 1e-3) / 1e9
     fp8 = c.wgt == "fp8_e4m3"
     out = {
@@ -519,7 +543,7 @@ def main():
         cf = CONFIGS["v3_fp8"]
         log("extra: the FP8 layer (T=32768, Zipf-skewed routing)")
         wf = make_weights(cf)
-        lf = MoeLayerGPU(cf, wf, gather=gather)
+        lf = MoeLayerGPU(cf, wf, gather=gather, keep_scores=False)
         xf = to_dev(make_x(cf, 0))
         bf = torch.from_numpy(wf.bias0.copy()).cuda()
         msf, stf = time_layer(lf, xf, bf, cf, args.steps, args.warmup)

@@ -16,7 +16,7 @@ import torch
 import oracle
 from biased_top_routing_amd import _lib as L
 from biased_top_routing_amd.runner import MoeLayerGPU, to_device
-from gpu_util import dev_f32, dev_i32, host, rel_inf, say
+from gpu_util import dev_f32, dev_i32, host, rel_inf, sample_tokens, say
 from workloads import MID, V3_FP8
 from workloads.inputs import f32_to_bf16_bits, make_weights, make_x, rng
 
@@ -372,18 +372,57 @@ def test_v3_fp8_full_size(v3_fp8):
     err = rel_inf(ysg, fe(qx, sx))
     say(f"  h codes equal to the oracle's: {same:.5f} (scale dev {dev:.1e}); y_perm segment err {err:.2e}")
     assert err < TOL
-    # shared expert on sampled tokens
-    rows = np.sort(rng(32, 1).choice(c.T, 8, replace=False))
+    # shared expert and the layer output on 256 sampled tokens (the last 16 of the batch and
+    # tokens of the largest, Zipf-hot, expert segment among them), teacher-forced on the
+    # GPU's selection; the skewed routing keeps the experts they touch to a few dozen
+    rows = sample_tokens(c.T, idx, 256, 32)
+    cache = {e: (lambda rq, fe=fe: fe(*rq))}
     fs = oracle.layer._Fp8Expert(w.ws_gate_up[0], w.ws_down[0])
+    cache[("shared", 0)] = lambda rq: fs(*rq)
     ref_s = fs(*oracle.quantize_rows_1x128(oracle.decode_act(xh[rows])))
     err = rel_inf(host(layer.y_shared)[rows], ref_s)
-    say(f"  y_shared sampled err {err:.2e}")
+    say(f"  y_shared err on {len(rows)} sampled tokens {err:.2e}")
     assert err < TOL
-    # the layer output of one sampled token, teacher-forced on the GPU's selection
-    r1 = rows[:1]
-    sel = np.take_along_axis(s_ora[r1].astype(np.float64), idx[r1].astype(np.int64), 1)
+    sel = np.take_along_axis(s_ora[rows].astype(np.float64), idx[rows].astype(np.int64), 1)
     w_rows = c.route_scale * sel / sel.sum(1, keepdims=True)
-    ref_y = oracle.sampled_forward(c, xh[r1], idx[r1], w_rows, w)
-    err = rel_inf(y[r1], ref_y)
+    say(f"  oracle layer output of {len(rows)} tokens over {len(np.unique(idx[rows]))} experts")
+    ref_y = oracle.sampled_forward(c, xh[rows], idx[rows], w_rows, w, experts_cache=cache)
+    err = rel_inf(y[rows], ref_y)
     say(f"  sampled y err {err:.2e}")
     assert err < TOL
+
+
+def test_v3_fp8_hundred_balance_steps(v3_fp8):
+    """The FP8 workload's 100 batches of routing + bias update (gamma = 1e-3, Zipf 1.5
+    preference), each batch a fresh x from the shared generator (a prefix of T = 8192 of
+    the full batch: the oracle routes every step's 8192 x 256 affinities in about a
+    quarter of a second, where the full 32768 tokens would take about 1.5 s per step).
+    Every step is checked teacher-forced and bit for bit: the oracle routes the GPU's
+    fp32 affinities with the bias the GPU holds, and the indices, the per-expert loads
+    and the updated bias must be identical; the gates within 2e-6."""
+    w, layer = v3_fp8
+    c = V3_FP8.with_(T=8192)
+    layer.alloc(c.T)
+    bias_h = w.bias0.copy()
+    bias = dev_f32(bias_h)
+    mean = c.T * c.k / c.E
+    ratios = []
+    for step in range(V3_FP8.steps):
+        say(f"v3 fp8 balance step {step} T={c.T}")
+        layer.forward(to_device(make_x(c, step, T=c.T)), bias, gamma=c.gamma)
+        torch.cuda.synchronize()
+        s_gpu = host(layer.scores)
+        idx = host(layer.topk_idx)
+        idx_o, w_o = oracle.route(s_gpu, bias_h, c.G, c.M, c.k, c.group_topr, c.route_scale)
+        assert (idx == idx_o).all(), step
+        np.testing.assert_allclose(host(layer.topk_w), w_o, rtol=2e-6, atol=1e-7)
+        counts = host(layer.counts)
+        assert (counts == np.bincount(idx.ravel(), minlength=c.E)).all(), step
+        bias_next = oracle.update_bias(bias_h, counts, c.T, c.k, c.gamma)
+        assert (host(bias).view(np.uint32) == bias_next.view(np.uint32)).all(), step
+        bias_h = bias_next
+        ratios.append(counts.max() / mean)
+    say(f"  max/mean load step 1 {ratios[0]:.2f}, step 100 {ratios[-1]:.2f}")
+    # the bias of the hottest expert fell by gamma every step (it is overloaded throughout)
+    hot = int(np.argmax(counts))
+    assert bias_h[hot] < w.bias0[hot] - 0.09

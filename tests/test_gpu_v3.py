@@ -7,7 +7,8 @@ permutation and the bias update are checked over the whole batch (bit-exact,
 teacher-forced on the GPU's fp32 scores; own-score index flips only at oracle
 near-ties below 1e-5).  Expert outputs are checked on samples the fp64 oracle can
 afford: whole segments of a few experts (y_perm), the shared expert on sampled
-tokens, and the full layer output on sampled tokens (normwise 2e-2)."""
+tokens, and the full layer output on 256 sampled tokens, among them the last 16 of the batch
+and tokens of the largest expert segment (every token at decode size; normwise 2e-2)."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +16,7 @@ import torch
 import oracle
 from biased_top_routing_amd import _lib as L
 from biased_top_routing_amd.runner import MoeLayerGPU, to_device
-from gpu_util import dev_f32, host, rel_inf, say
+from gpu_util import dev_f32, host, rel_inf, sample_tokens, say
 from workloads import V3_PREFILL
 from oracle.layer import decode_act
 from workloads.inputs import f32_to_bf16_bits, make_weights, make_x, rng
@@ -87,8 +88,9 @@ def _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok, experts
         ref = oracle.swiglu(oracle.decode_act(xh[perm[lo:hi] // c.k]), oracle.decode_act(w.w_gate_up[e]),
                             oracle.decode_act(w.w_down[e]))
         assert rel_inf(host(yp[lo:hi]), ref) < 2e-2
-    # shared expert and full layer output on sampled tokens
-    rows = np.sort(rng(7, n_tok).choice(len(xh), n_tok, replace=False))
+    # shared expert and full layer output on sampled tokens (the last rows of the batch
+    # and tokens of the largest expert segment among them)
+    rows = sample_tokens(len(xh), idx, n_tok, 7)
     ref_sh = oracle.shared_ffn(oracle.decode_act(xh[rows]), [oracle.decode_act(a) for a in w.ws_gate_up],
                                [oracle.decode_act(a) for a in w.ws_down])
     assert rel_inf(host(layer.y_shared)[rows], ref_sh) < 2e-2
@@ -106,7 +108,8 @@ def test_v3_prefill_full_size(v3):
     c = V3_PREFILL
     xh, bias_h, bias_next, y = _run(c, w, layer, c.T, 0)
     s_ora, idx, offsets, perm = _check_routing(c, c.T, w, layer, xh, bias_h, bias_next)
-    _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok=6, experts=(0, 131, 255))
+    _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok=256,
+                   experts=(0, 131, 255, int(np.argmax(np.diff(offsets)))))
 
 
 def test_v3_decode_full_size(v3):
@@ -114,7 +117,8 @@ def test_v3_decode_full_size(v3):
     c = V3_PREFILL.with_(name="v3_decode_bf16", T=128)
     xh, bias_h, bias_next, y = _run(c, w, layer, c.T, 3)
     s_ora, idx, offsets, perm = _check_routing(c, c.T, w, layer, xh, bias_h, bias_next)
-    _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok=6, experts=(int(idx[0, 0]),))
+    _check_outputs(c, w, layer, xh, s_ora, idx, offsets, perm, y, n_tok=c.T,
+                   experts=(int(idx[0, 0]), int(np.argmax(np.diff(offsets)))))
 
 
 def test_v3_prefill_gather_bit_exact(v3):
