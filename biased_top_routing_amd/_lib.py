@@ -19,7 +19,7 @@ MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORES_IN = 1
 MOE_FFN_ALL, MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1, 2
-MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_FFN_BWD, MOE_WS_ROUTE_BWD = 1, 2, 3, 4
+MOE_WS_DISPATCH, MOE_WS_FFN, MOE_WS_FFN_BWD, MOE_WS_ROUTE_BWD, MOE_WS_ROUTE = 1, 2, 3, 4, 5
 MOE_WSP_H, MOE_WSP_H_SCALE, MOE_WSP_H_SHARED, MOE_WSP_H_SHARED_SCALE = 0, 1, 2, 3
 _DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8_e4m3": MOE_FP8_E4M3}
 
@@ -63,7 +63,7 @@ def lib() -> ctypes.CDLL:
         vp, i32, u32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
         cfgp = ctypes.POINTER(MoeCfg)
         sig = {
-            "moe_route": [cfgp, vp, vp, vp, vp, vp, u32, vp, vp, vp],
+            "moe_route": [cfgp, vp, vp, vp, vp, vp, u32, vp, vp, vp, sz, vp],
             "moe_dispatch": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "moe_expert_ffn": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp, sz,
                                ctypes.c_int, vp],
@@ -148,9 +148,10 @@ def _check(name: str, st: int) -> None:
         raise MoeError(name, st)
 
 
-def moe_route(cfg, x, w_router, logit_offset, bias, scores, flags, topk_idx, topk_w, stream=None):
+def moe_route(cfg, x, w_router, logit_offset, bias, scores, flags, topk_idx, topk_w, ws=None, stream=None):
     _check("moe_route", lib().moe_route(ctypes.byref(cfg), _p(x), _p(w_router), _p(logit_offset), _p(bias),
-                                        _p(scores), flags, _p(topk_idx), _p(topk_w), _s(stream)))
+                                        _p(scores), flags, _p(topk_idx), _p(topk_w), _p(ws), _nbytes(ws),
+                                        _s(stream)))
 
 
 def moe_dispatch(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale, ws, stream=None):

@@ -49,6 +49,7 @@ using namespace moe;
 
 extern "C" size_t moe_workspace_bytes(const moe_cfg* cfg, int which) {
   if (validate_cfg(cfg) != MOE_OK) return 0;
+  if (which == MOE_WS_ROUTE) return route_ws_bytes(cfg);
   if (which == MOE_WS_DISPATCH) return dispatch_ws_bytes(cfg);
   if (which == MOE_WS_FFN) return FfnLayout(cfg).total;
   if (which == MOE_WS_FFN_BWD) return FfnBwdLayout(cfg).total;

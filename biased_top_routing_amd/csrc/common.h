@@ -23,6 +23,12 @@ inline moe_status launch_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// moe_route's workspace: room for the [T, E] fp32 affinities when the caller
+// passes no `scores` (at least 256 bytes, so that a size of 0 means an invalid cfg)
+inline size_t route_ws_bytes(const moe_cfg* c) {
+  const size_t b = (size_t)c->T * c->E * sizeof(float);
+  return align_up(b < 256 ? 256 : b, 256);
+}
 
 // ---------------------------------------------------------------- device side
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) {

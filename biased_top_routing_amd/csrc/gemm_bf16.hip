@@ -26,13 +26,17 @@
 #include "ffn_layout.h"
 #include "gemm_common.h"
 #include "kernels.h"
+#include "route_topk.h"
 
 namespace moe {
 
 // kGateUpGU: the gate/up GEMM storing the gate and up outputs themselves
 // (recomputed for the backward pass) instead of h; kGateUpSave: storing h and
 // the gate and up outputs (a forward pass that keeps them for the backward).
-enum { kRouter = 0, kGateUp = 1, kDown = 2, kGateUpGU = 3, kGateUpSave = 4 };
+// kRouterTopk: the router GEMM whose epilogue leaves the tile's affinities in
+// LDS (and in `scores` when given) for the workgroup's top-k.
+enum { kRouter = 0, kGateUp = 1, kDown = 2, kGateUpGU = 3, kGateUpSave = 4, kRouterTopk = 5 };
+constexpr bool is_router(int mode) { return mode == kRouter || mode == kRouterTopk; }
 constexpr bool is_gate_up(int mode) { return mode == kGateUp || mode == kGateUpGU || mode == kGateUpSave; }
 
 
@@ -51,6 +55,11 @@ struct GemmParams {
   const TileDesc* tiles;
   const int32_t* ntiles;
   const int32_t* perm;      // gate/up: non-null -> routed rows gathered from a_shared
+  const float* bias;        // router top-k: routing bias [E]
+  int32_t* topk_idx;        // router top-k: [T, k] out
+  float* topk_w;            //   [T, k] out
+  int G, M;                 //   expert groups, groups per token
+  float route_scale;
   int T, H, E, S, I, k;
 };
 
@@ -73,7 +82,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const bool shared = (MODE != kRouter) && seg == p.E;
+  const bool shared = !is_router(MODE) && seg == p.E;
   // Routed gate/up rows gathered straight from x: row row0 + r of the
   // expert-sorted order is token perm[row0 + r] / k (dispatch's row copy
   // folded into the operand loads).
@@ -86,7 +95,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
     A = shared ? p.a_shared : p.a_routed;
     lda = shared ? p.S * p.I : p.I;
   } else {
-    A = (MODE == kRouter || shared || gather) ? p.a_shared : p.a_routed;
+    A = (is_router(MODE) || shared || gather) ? p.a_shared : p.a_routed;
     lda = p.H;
   }
   const int K = lda;
@@ -97,7 +106,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   int ldw;
   int64_t seg_kstride = 0;   // down, shared: next shared expert's W_d every I columns of K
   int ncols;                 // valid output columns of this GEMM (h columns for gate/up)
-  if constexpr (MODE == kRouter) {
+  if constexpr (is_router(MODE)) {
     W = p.w_routed;
     ldw = p.H;
     ncols = p.E;
@@ -147,7 +156,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   // SGPR offset.  Accesses past the described range read as zero.
   // (the host checks that a segment's weights stay below 2 GiB)
   int w_bytes;
-  if constexpr (MODE == kRouter) w_bytes = p.E * p.H * 2;
+  if constexpr (is_router(MODE)) w_bytes = p.E * p.H * 2;
   else if constexpr (is_gate_up(MODE)) w_bytes = (shared ? p.S : 1) * 2 * p.I * p.H * 2;
   else w_bytes = (shared ? p.S : 1) * p.H * p.I * 2;
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, a_rows * lda * 2);
@@ -265,6 +274,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] holds C[i][j] with j = lane % 32 and
   // i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 inside the 32 x 32 block.
+  // kRouterTopk reuses the LDS ring for the [BM][BN] fp32 affinities: every
+  // wavefront must be done with its last slice first.
+  if constexpr (MODE == kRouterTopk) __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -295,6 +307,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
         for (int ni = 0; ni < NI; ++ni) {
           const int col = nt * BN + wn * NI * 32 + ni * 32 + lr;
           if (col < ncols) out[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
+        }
+      } else if constexpr (MODE == kRouterTopk) {
+        // the tile holds every expert of its tokens (nt == 0, BN >= E)
+        float* sl = reinterpret_cast<float*>(lds);
+        float* out = static_cast<float*>(p.out_routed);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = wn * NI * 32 + ni * 32 + lr;
+          float sv = 0.f;
+          if (col < ncols) {
+            const float l = acc[mi][ni][r] + (p.offset ? p.offset[col] : 0.f);
+            sv = 1.0f / (1.0f + expf(-l));
+            if (out) out[row * ncols + col] = sv;
+          }
+          sl[i * BN + col] = sv;
         }
       } else {
         float* out = static_cast<float*>(p.out_routed);
@@ -410,19 +437,41 @@ __global__ __launch_bounds__(64 * kRsWaves) void router_splitk_kernel(const bf16
 #endif
 }
 
-moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
-                              const float* offset, float* scores, hipStream_t st) {
-  GemmParams p{};
-  p.a_shared = x;
-  p.w_routed = w_router;
-  p.offset = offset;
-  p.out_routed = scores;
-  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-  // Large batches: every token tile re-reads its columns of the router weight
-  // from L2, so the tile is as large as the batch allows while the grid still
-  // covers every CU: 256 x 256 and 128 x 256 for large batches, 128 x 128 at
-  // T = 16384 (two column tiles of 128 experts: 3.5 instead of 4.6 MB of operand
-  // loads per tile against 64 x 256, measured 14% faster), else 64 x 256.
+// Router GEMM with the whole routing step in its epilogue, for tiles that hold
+// every expert of their tokens (BN >= E): the tile's affinities
+// s = sigmoid(x W_r^T + o) go to LDS (and to `scores` when given), then the
+// workgroup's 16-lane slices run the biased group-limited top-k of its tokens
+// from LDS (topk16_token, the per-token code of the standalone top-k kernel),
+// so the [T, E] affinities need not be written and read back.  The GEMM part
+// adds the K slices in the order of the standalone router GEMM, so its
+// affinities, and with them the selection, are the same bit for bit.
+template <int EPL, int TOPR, int WM, int WN, int MI, int NI, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void router_topk_kernel(GemmParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BM = WM * MI * 32, BN = WN * NI * 32;
+  constexpr int RING = STAGES * (BM + BN) * BK, SCO = 2 * BM * BN;   // in bf16 elements
+  constexpr int TPP = 64 * WM * WN / 16;                            // tokens per pass
+  static_assert(16 * EPL <= BN && BM % TPP == 0, "a tile holds every expert; whole passes");
+  __shared__ __attribute__((aligned(16))) bf16_t lds[RING > SCO ? RING : SCO];
+  const int row0 = blockIdx.x * BM;
+  const int rows = min(BM, p.T - row0);
+  gemm_tile<kRouterTopk, WM, WN, MI, NI, BK, STAGES>(p, lds, 0, row0, rows, 0);
+  __syncthreads();
+  const float* sl = reinterpret_cast<const float*>(lds);
+  const int l16 = threadIdx.x & 15;
+  float b[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) b[j] = p.bias[l16 * EPL + j];
+  for (int tt = threadIdx.x / 16; tt < BM; tt += TPP) {   // the same trip count on every lane
+    const bool valid = tt < rows;
+    const int64_t t = row0 + (valid ? tt : 0);
+    topk16_token<EPL, TOPR>(sl + tt * BN, b, valid, p.G, p.M, p.k, p.route_scale, p.topk_idx + t * p.k,
+                            p.topk_w + t * p.k);
+  }
+#endif
+}
+
+static int cu_count() {
   static int n_cu = 0;
   if (n_cu == 0) {
     int dev = 0, n = 0;
@@ -431,35 +480,121 @@ moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w
       n = 256;
     n_cu = n;
   }
-  auto tiles = [&](auto cfg) {
-    using RT = decltype(cfg);
-    return ((int64_t)c->T + RT::BM - 1) / RT::BM * (((int64_t)c->E + RT::BN - 1) / RT::BN);
-  };
+  return n_cu;
+}
+
+// Router kernel and tile by batch size.  Small batches: the split-K kernel with
+// 16 x 16 tiles while there are at most two per CU, else with 32 x 32 tiles
+// while there are at most two per CU (route stage with a cache flush, against
+// 64 x 256 tiles: E = 256, T = 128 100 -> 27 us, T = 2048 99 -> 82 us; E = 64,
+// T = 4096 33 -> 23 us).  Larger batches: every token tile re-reads its columns
+// of the router weight from L2, so the tile is as large as the batch allows
+// while the grid still covers every CU: 256 x 256 and 128 x 256 for large
+// batches, 128 x 128 at T = 16384 with E = 256 (two column tiles of 128
+// experts: 3.5 instead of 4.6 MB of operand loads per tile against 64 x 256,
+// measured 14% faster), else 64 x 256.
+enum RouterTile { kRtSplit16, kRtSplit32, kRt256, kRt128, kRt128N, kRt64 };
+using RT256 = TileCfg<MOE_RT256_TILE>;
+using RT128 = TileCfg<MOE_RT128_TILE>;
+using RT128N = TileCfg<MOE_RT128N_TILE>;
+using RT64 = TileCfg<MOE_RT_TILE>;
+
+static RouterTile router_tile(const moe_cfg* c) {
+  const int64_t n_cu = cu_count();
+  auto tiles = [&](int bm, int bn) { return ((int64_t)c->T + bm - 1) / bm * (((int64_t)c->E + bn - 1) / bn); };
+  if (tiles(16, 16) <= 2 * n_cu) return kRtSplit16;
+  if (tiles(32, 32) <= 2 * n_cu) return kRtSplit32;
+  if (tiles(RT256::BM, RT256::BN) >= n_cu) return kRt256;
+  if (tiles(RT128::BM, RT128::BN) >= n_cu) return kRt128;
+  if (tiles(RT128N::BM, RT128N::BN) >= n_cu) return kRt128N;
+  return kRt64;
+}
+
+// The fused kernel runs where the two-kernel path would use 64-token tiles
+// anyway (mid-size batches: E = 256 from T = 2049 to 16383); there it saves the
+// affinities' round trip and a launch.  Larger batches keep the larger tiles of
+// the two-kernel path: with a cache flush, the fused 64 x 256 tiles took
+// 0.143 / 0.439 / 1.60 ms against 0.133 / 0.319 / 1.18 ms at T = 16384 / 65536
+// / 262144 (every tile re-reads the whole 3.7 MB router weight).
+#ifndef MOE_ROUTE_FUSED
+#define MOE_ROUTE_FUSED 1
+#endif
+bool router_topk_fusable(const moe_cfg* c) {
+  if (!MOE_ROUTE_FUSED || c->act != MOE_BF16 || !topk16_fits(c) || c->E > 256) return false;
+  const int epl = c->E / 16;
+  return (epl == 1 || epl == 2 || epl == 4 || epl == 8 || epl == 16) && router_tile(c) == kRt64;
+}
+
+template <int EPL, int TOPR>
+static void launch_router_topk_r(const moe_cfg* c, const GemmParams& p, hipStream_t st) {
+  const dim3 grid((unsigned)((c->T + 63) / 64));
+  if constexpr (EPL <= 8)   // 64 tokens x 128 experts
+    hipLaunchKernelGGL((router_topk_kernel<EPL, TOPR, 2, 4, 1, 1, 64, 3>), grid, dim3(512), 0, st, p);
+  else                      // 64 tokens x 256 experts
+    hipLaunchKernelGGL((router_topk_kernel<EPL, TOPR, 2, 4, 1, 2, 64, 3>), grid, dim3(512), 0, st, p);
+}
+
+template <int EPL>
+static void launch_router_topk_e(const moe_cfg* c, const GemmParams& p, hipStream_t st) {
+  switch (c->group_topr) {
+    case 1: launch_router_topk_r<EPL, 1>(c, p, st); break;
+    case 2: launch_router_topk_r<EPL, 2>(c, p, st); break;
+    case 3: launch_router_topk_r<EPL, 3>(c, p, st); break;
+    default: launch_router_topk_r<EPL, 4>(c, p, st); break;
+  }
+}
+
+moe_status launch_router_topk_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router, const float* offset,
+                                   const float* bias, float* scores, int32_t* idx, float* w, hipStream_t st) {
+  if (!router_topk_fusable(c)) return MOE_ERR_UNSUPPORTED;
+  GemmParams p{};
+  p.a_shared = x;
+  p.w_routed = w_router;
+  p.offset = offset;
+  p.out_routed = scores;
+  p.bias = bias;
+  p.topk_idx = idx;
+  p.topk_w = w;
+  p.G = c->G; p.M = c->M; p.route_scale = c->route_scale;
+  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
+  switch (c->E / 16) {
+    case 1: launch_router_topk_e<1>(c, p, st); break;
+    case 2: launch_router_topk_e<2>(c, p, st); break;
+    case 4: launch_router_topk_e<4>(c, p, st); break;
+    case 8: launch_router_topk_e<8>(c, p, st); break;
+    default: launch_router_topk_e<16>(c, p, st); break;
+  }
+  return launch_status();
+}
+
+moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
+                              const float* offset, float* scores, hipStream_t st) {
+  GemmParams p{};
+  p.a_shared = x;
+  p.w_routed = w_router;
+  p.offset = offset;
+  p.out_routed = scores;
+  p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
   auto launch = [&](auto cfg) {
     using RT = decltype(cfg);
     const dim3 grid((unsigned)((c->T + RT::BM - 1) / RT::BM), (unsigned)((c->E + RT::BN - 1) / RT::BN));
     hipLaunchKernelGGL((gemm_bf16_kernel<kRouter, RT::WM, RT::WN, RT::MI, RT::NI, RT::BK, RT::STAGES, RT::OCC>), grid,
                        dim3(64 * RT::WM * RT::WN), 0, st, p);
   };
-  using RT256 = TileCfg<MOE_RT256_TILE>;
-  using RT128 = TileCfg<MOE_RT128_TILE>;
-  using RT128N = TileCfg<MOE_RT128N_TILE>;
-  // Small batches: the split-K kernel with 16 x 16 tiles while there are at
-  // most two per CU, else with 32 x 32 tiles while there are at most two per CU
-  // (route stage with a cache flush, against 64 x 256 tiles: E = 256, T = 128
-  // 100 -> 27 us, T = 2048 99 -> 82 us; E = 64, T = 4096 33 -> 23 us).
-  const int64_t t16 = ((int64_t)c->T + 15) / 16 * ((c->E + 15) / 16);
-  const int64_t t32 = ((int64_t)c->T + 31) / 32 * ((c->E + 31) / 32);
-  if (t16 <= 2 * n_cu)
-    hipLaunchKernelGGL(router_splitk_kernel<16>, dim3((unsigned)((c->T + 15) / 16), (unsigned)((c->E + 15) / 16)),
-                       dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
-  else if (t32 <= 2 * n_cu)
-    hipLaunchKernelGGL(router_splitk_kernel<32>, dim3((unsigned)((c->T + 31) / 32), (unsigned)((c->E + 31) / 32)),
-                       dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
-  else if (tiles(RT256{}) >= n_cu) launch(RT256{});
-  else if (tiles(RT128{}) >= n_cu) launch(RT128{});
-  else if (tiles(RT128N{}) >= n_cu) launch(RT128N{});
-  else launch(TileCfg<MOE_RT_TILE>{});
+  switch (router_tile(c)) {
+    case kRtSplit16:
+      hipLaunchKernelGGL(router_splitk_kernel<16>, dim3((unsigned)((c->T + 15) / 16), (unsigned)((c->E + 15) / 16)),
+                         dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
+      break;
+    case kRtSplit32:
+      hipLaunchKernelGGL(router_splitk_kernel<32>, dim3((unsigned)((c->T + 31) / 32), (unsigned)((c->E + 31) / 32)),
+                         dim3(64 * kRsWaves), 0, st, x, w_router, offset, scores, c->T, c->H, c->E);
+      break;
+    case kRt256: launch(RT256{}); break;
+    case kRt128: launch(RT128{}); break;
+    case kRt128N: launch(RT128N{}); break;
+    default: launch(RT64{}); break;
+  }
   return launch_status();
 }
 

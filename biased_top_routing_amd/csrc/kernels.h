@@ -11,6 +11,12 @@ moe_status launch_route_topk(const moe_cfg* c, const float* scores, const float*
 moe_status launch_router_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router,
                               const float* offset, float* scores, hipStream_t st);
 
+// Router GEMM + sigmoid + biased group-limited top-k + gates in one kernel
+// (scores may be null); router_topk_fusable tells whether it covers c.
+bool router_topk_fusable(const moe_cfg* c);
+moe_status launch_router_topk_bf16(const moe_cfg* c, const bf16_t* x, const bf16_t* w_router, const float* offset,
+                                   const float* bias, float* scores, int32_t* idx, float* w, hipStream_t st);
+
 // x_perm: the expert-sorted rows written by dispatch; or perm != nullptr: the
 // routed gate/up rows are gathered from x (row p = token perm[p] / k) and
 // x_perm is not read.  saved != nullptr: the gate/up GEMM also stores its gate

@@ -9,6 +9,7 @@
 // groups, the one-GPU form of the pages' limit of M nodes per token.
 #include "common.h"
 #include "kernels.h"
+#include "route_topk.h"
 
 namespace moe {
 
@@ -154,73 +155,14 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 }
 
 // Fast form for E = 16 * EPL with groups of whole lanes: one token per 16
-// lanes (four per wavefront), lane l of a slice holds experts [l*EPL, (l+1)*EPL)
-// in registers and every group spans LG = (E/G)/EPL consecutive lanes (a power
-// of two).  No LDS and no barrier:
-//   each lane keeps the top-TOPR biased scores of its experts; the LG lanes of
-//   a group merge their lists with xor shuffles, so each holds the group's
-//   top-TOPR and adds them largest first (fp32), as the reference does;
-//   a group's rank = number of groups with a larger score or an equal score
-//   and a lower index (group scores gathered by shuffles); chosen = rank < M;
-//   k rounds of a 16-lane max over 64-bit keys (order key of q, ~expert), the
-//   affinity s of the round's winner travelling with its key.
-// Cross-lane moves inside a row of 16 lanes with DPP (VALU rate, no LDS):
-// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at xor 1 and xor 2; the
-// half-row mirror pairs lane i with 7-i and the row mirror lane i with 15-i.
-// Applied in this order, each step pairs lanes whose partial results cover
-// disjoint lane sets, so after 1/2/3/4 steps every lane holds the result over
-// its 2/4/8/16-lane block.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
-}
-
-// One step of the (64-bit key, value) max: keep the larger key and its value.
-template <int CTRL>
-__device__ __forceinline__ void max_step(uint64_t& best, float& val) {
-  const uint32_t lo = dpp_u32<CTRL>((uint32_t)best);
-  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(best >> 32));
-  const float ov = dpp_f32<CTRL>(val);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  const bool gt = o > best;
-  best = gt ? o : best;
-  val = gt ? ov : val;
-}
-
-// Merge the partner's top-R list into this lane's (both descending).
-template <int CTRL, int R>
-__device__ __forceinline__ void merge_step(float (&top)[R]) {
-  float other[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) other[i] = dpp_f32<CTRL>(top[i]);
-#pragma unroll
-  for (int i2 = 0; i2 < R; ++i2) {
-    float v = other[i2];
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float hi = fmaxf(top[i], v), lo = fminf(top[i], v);
-      top[i] = hi;
-      v = lo;
-    }
-  }
-}
-
+// lanes (four per wavefront), no LDS and no barrier; the per-token work is
+// topk16_token (route_topk.h), which the fused router kernel runs as well.
 template <int EPL, int TOPR>
 __global__ __launch_bounds__(256) void route_topk16_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, int T, int E, int G, int M,
     int k, float scale, int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   constexpr int LPT = 16;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int sl = lane & (LPT - 1);
-  const int slice0 = lane & ~(LPT - 1);                   // first lane of this token's slice
-  const int LG = (E / G) / EPL;                           // lanes per group
-  const int grp = sl / LG;
+  const int sl = threadIdx.x & (LPT - 1);
   float b[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) b[j] = bias[sl * EPL + j];
@@ -230,100 +172,9 @@ __global__ __launch_bounds__(256) void route_topk16_kernel(
     // (the loop condition keeps whole wavefronts iterating together; lanes of a
     //  token past T load nothing and store nothing)
     const bool valid = t < T;
-    float s[EPL], q[EPL];
-    const float* row = scores + (valid ? t : 0) * E + sl * EPL;
-    if constexpr (EPL % 4 == 0) {
-#pragma unroll
-      for (int j = 0; j < EPL; j += 4) {
-        const float4 v = valid ? *reinterpret_cast<const float4*>(row + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-        s[j] = v.x; s[j + 1] = v.y; s[j + 2] = v.z; s[j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) s[j] = valid ? row[j] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) q[j] = s[j] + b[j];
-    // ---- group score: top-TOPR of the group, summed largest first
-    float top[TOPR];
-#pragma unroll
-    for (int i = 0; i < TOPR; ++i) top[i] = -__builtin_huge_valf();
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      float v = q[j];
-#pragma unroll
-      for (int i = 0; i < TOPR; ++i) {
-        const float hi = fmaxf(top[i], v), lo = fminf(top[i], v);
-        top[i] = hi;
-        v = lo;
-      }
-    }
-    // the LG lanes of a group (an aligned block of 1, 2, 4, 8 or 16 lanes)
-    if (LG >= 2) merge_step<kDppXor1>(top);
-    if (LG >= 4) merge_step<kDppXor2>(top);
-    if (LG >= 8) merge_step<kDppHalfMirror>(top);
-    if (LG >= 16) merge_step<kDppMirror>(top);
-    float gs = top[0];
-#pragma unroll
-    for (int i = 1; i < TOPR; ++i) gs = gs + top[i];
-    // ---- group rank among the G groups of this token
-    int rank = 0;
-    for (int h = 0; h < G; ++h) {
-      const float o = __shfl(gs, slice0 + h * LG);
-      rank += (o > gs) || (o == gs && h < grp);
-    }
-    const bool chosen = rank < M;
-    // ---- k rounds of the 16-lane max.  Keys are the 32-bit order keys of q
-    // (0 = not selectable: a non-chosen group, a cleared winner, a token past
-    // T).  A round takes the largest key (per-lane max, then a 16-lane DPP
-    // max), then among the lanes holding it the lowest expert index (DPP min),
-    // so ties go to the lower index; the winner clears its entry.  The gate
-    // values are read back from the score row at the end.
-    uint32_t key[EPL];
-#pragma unroll
-    for (int j = 0; j < EPL; ++j) key[j] = (valid && chosen) ? float_order_key(q[j]) : 0u;
-    int my_e = 0;
-    for (int r = 0; r < k; ++r) {
-      uint32_t m = key[0];
-#pragma unroll
-      for (int j = 1; j < EPL; ++j) m = max(m, key[j]);
-      m = max(m, dpp_u32<kDppXor1>(m));
-      m = max(m, dpp_u32<kDppXor2>(m));
-      m = max(m, dpp_u32<kDppHalfMirror>(m));
-      m = max(m, dpp_u32<kDppMirror>(m));
-      int jl = EPL;                                   // lowest local position holding the max
-#pragma unroll
-      for (int j = EPL - 1; j >= 0; --j) jl = key[j] == m ? j : jl;
-      uint32_t we = jl < EPL ? (uint32_t)(sl * EPL + jl) : 0xFFFFFFFFu;
-      we = min(we, dpp_u32<kDppXor1>(we));
-      we = min(we, dpp_u32<kDppXor2>(we));
-      we = min(we, dpp_u32<kDppHalfMirror>(we));
-      we = min(we, dpp_u32<kDppMirror>(we));
-      const int jw = (int)we - sl * EPL;              // in [0, EPL) on the winning lane only
-#pragma unroll
-      for (int j = 0; j < EPL; ++j) key[j] = j == jw ? 0u : key[j];
-      if (sl == r) my_e = (int)we;
-    }
-    const float my_s = (valid && sl < k) ? row[my_e - sl * EPL] : 0.f;
-    float tot = my_s;
-    tot += dpp_f32<kDppXor1>(tot);
-    tot += dpp_f32<kDppXor2>(tot);
-    tot += dpp_f32<kDppHalfMirror>(tot);
-    tot += dpp_f32<kDppMirror>(tot);
-    if (valid && sl < k) {
-      idx_out[t * k + sl] = my_e;
-      w_out[t * k + sl] = scale * my_s / tot;
-    }
+    const int64_t tr = valid ? t : 0;
+    topk16_token<EPL, TOPR>(scores + tr * E, b, valid, G, M, k, scale, idx_out + tr * k, w_out + tr * k);
   }
-}
-
-// E = 16 * EPL, groups of whole lanes (LG a power of two), k <= 16, top-r <= 4.
-static bool topk16_fits(const moe_cfg* c) {
-  if (c->E % 16 || c->E / 16 > 16 || c->k > 16 || c->group_topr > 4) return false;
-  const int epl = c->E / 16, gsz = c->E / c->G;
-  if (gsz % epl) return false;
-  const int lg = gsz / epl;
-  return (lg & (lg - 1)) == 0;
 }
 
 template <int EPL, int TOPR>
@@ -384,26 +235,36 @@ using namespace moe;
 
 extern "C" moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
                                 const float* logit_offset, const float* bias, float* scores,
-                                uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream) {
+                                uint32_t flags, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                                void* stream) {
   moe_status st = validate_cfg(cfg);
   if (st != MOE_OK) return st;
   if (flags & ~MOE_SCORES_IN) return MOE_ERR_UNSUPPORTED;
   const bool scores_in = flags & MOE_SCORES_IN;
-  if (!bias || !scores || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (!bias || !topk_idx || !topk_w) return MOE_ERR_NULL;
+  if (scores_in && !scores) return MOE_ERR_NULL;
   if (!scores_in && (!x || !w_router)) return MOE_ERR_NULL;
+  // without `scores` the affinities are staged in the workspace, unless the
+  // fused kernel keeps them in LDS (the workspace is still required, so that a
+  // caller's arguments are valid on every device)
+  if (!scores && (!ws || ws_bytes < route_ws_bytes(cfg))) return MOE_ERR_WORKSPACE;
   if (cfg->T == 0) return MOE_OK;
   hipStream_t s = as_stream(stream);
+  if (!scores_in && router_topk_fusable(cfg))
+    return launch_router_topk_bf16(cfg, (const bf16_t*)x, (const bf16_t*)w_router, logit_offset, bias, scores,
+                                   topk_idx, topk_w, s);
+  float* sc = scores ? scores : static_cast<float*>(ws);
   if (!scores_in) {
     if (cfg->act == MOE_F32) {
       const int64_t n = (int64_t)cfg->T * cfg->E;
       hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                         (const float*)x, (const float*)w_router, logit_offset, scores, cfg->T,
+                         (const float*)x, (const float*)w_router, logit_offset, sc, cfg->T,
                          cfg->H, cfg->E);
       if ((st = launch_status()) != MOE_OK) return st;
     } else {
-      st = launch_router_bf16(cfg, (const bf16_t*)x, (const bf16_t*)w_router, logit_offset, scores, s);
+      st = launch_router_bf16(cfg, (const bf16_t*)x, (const bf16_t*)w_router, logit_offset, sc, s);
       if (st != MOE_OK) return st;
     }
   }
-  return launch_route_topk(cfg, scores, bias, topk_idx, topk_w, s);
+  return launch_route_topk(cfg, sc, bias, topk_idx, topk_w, s);
 }

@@ -8,7 +8,8 @@ the indices and the routed gate/up GEMM reads its rows from x through perm
 (moe_expert_ffn_gather); no x_perm is allocated.  With save_gu=True (bf16),
 the forward pass keeps the gate and up outputs (moe_expert_ffn_save) and the
 backward pass starts from them (moe_expert_ffn_backward_saved) instead of
-recomputing the gate/up GEMM.
+recomputing the gate/up GEMM.  With keep_scores=False, moe_route writes no
+[T, E] affinities (a forward pass that needs no router gradient).
 """
 from __future__ import annotations
 
@@ -29,11 +30,12 @@ def to_device(arr, device="cuda"):
 
 
 class MoeLayerGPU:
-    def __init__(self, cfg, weights, T=None, device="cuda", gather=False, save_gu=False):
+    def __init__(self, cfg, weights, T=None, device="cuda", gather=False, save_gu=False, keep_scores=True):
         self.c = cfg
         self.device = device
         self.gather = gather
         self.save_gu = save_gu
+        self.keep_scores = keep_scores
         self.fp8 = cfg.wgt == "fp8_e4m3"
         self.act_dtype = torch.float32 if cfg.act == "f32" else torch.bfloat16
         dev = lambda a: to_device(a, device)
@@ -71,7 +73,10 @@ class MoeLayerGPU:
         self.cfg = L.cfg_from(c, T=T)
         d, P = self.device, T * c.k
         f32, i32 = torch.float32, torch.int32
+        # the [T, E] affinities (the backward pass reads them); without them moe_route
+        # gets a workspace instead and a fused router kernel keeps them on chip
         self.scores = torch.empty((T, c.E), dtype=f32, device=d)
+        self.ws_route = torch.empty(L.moe_workspace_bytes(self.cfg, L.MOE_WS_ROUTE), dtype=torch.uint8, device=d)
         self.topk_idx = torch.empty((T, c.k), dtype=i32, device=d)
         self.topk_w = torch.empty((T, c.k), dtype=f32, device=d)
         self.counts = torch.empty(c.E, dtype=i32, device=d)
@@ -102,8 +107,10 @@ class MoeLayerGPU:
 
     # ---------------------------------------------------------------- the five calls
     def route(self, x, bias, scores_in=False):
-        L.moe_route(self.cfg, x, self.w_router, self.logit_offset, bias, self.scores,
-                    L.MOE_SCORES_IN if scores_in else 0, self.topk_idx, self.topk_w)
+        keep = self.keep_scores or scores_in
+        L.moe_route(self.cfg, x, self.w_router, self.logit_offset, bias, self.scores if keep else None,
+                    L.MOE_SCORES_IN if scores_in else 0, self.topk_idx, self.topk_w,
+                    None if keep else self.ws_route)
 
     def dispatch(self, x):
         L.moe_dispatch(self.cfg, self.topk_idx, x, self.counts, self.offsets, self.perm, self.inv, self.x_perm,

@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -93,20 +93,35 @@ typedef struct {
  *  logit_offset [E] fp32 added to the logits before the sigmoid, or NULL
  *  bias         [E] fp32 routing bias b
  *  scores       [T, E] fp32: output s = sigmoid(x w_router^T + o), or the input
- *               affinities with MOE_SCORES_IN
+ *               affinities with MOE_SCORES_IN; may be NULL without MOE_SCORES_IN
+ *               (the affinities are then not written: a forward pass that needs
+ *               no router gradient)
  *  topk_idx     [T, k] int32 out: selected experts, ordered by s + b descending,
  *               ties to the lower expert index (-0.0 ranks as +0.0)
  *  topk_w       [T, k] fp32 out: route_scale * s_j / sum_j s_j
+ *  ws, ws_bytes workspace of at least moe_workspace_bytes(cfg, MOE_WS_ROUTE)
+ *               bytes, required when scores is NULL (it stages the affinities
+ *               where no kernel keeps them on chip); ignored otherwise (may be NULL)
  * Groups are chosen first (the M largest group scores, ties to the lower group),
  * then the k largest s + b among the experts of the chosen groups.
  * NaN scores give unspecified indices.
+ * For mid-size bf16 batches (too large for the split-K router, too small for
+ * router tiles of 128 tokens to fill the chip; E = 256: 2049 <= T < 16384) with
+ * E = 16, 32, 64, 128 or 256 in groups of a power-of-two number of 16-lane
+ * slices, k <= 16 and group_topr <= 4, one kernel runs the router GEMM and the
+ * whole selection (the affinities stay in LDS, and are also written when scores
+ * is given); it selects with the same code as the MOE_SCORES_IN path, so
+ * routing its own affinities again with MOE_SCORES_IN gives the same indices
+ * and gates.
  * The router GEMM sums in a fixed order per batch size (repeated calls give
  * identical bits); small and large batches use different kernels, so the last
  * bits of a token's affinities can depend on T.
+ * MOE_ERR_WORKSPACE: scores is NULL and ws is NULL or too small.
  */
 moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
                      const float* logit_offset, const float* bias, float* scores,
-                     uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream);
+                     uint32_t flags, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /*
  * moe_dispatch - per-expert loads and the expert-sorted permutation of the
@@ -371,6 +386,7 @@ moe_status moe_dispatch_backward(const moe_cfg* cfg, const void* dx_perm, const 
                                  const float* dx_router, const int32_t* inv, void* dx, void* stream);
 
 /* Workspace kinds for moe_workspace_bytes */
+#define MOE_WS_ROUTE 5
 #define MOE_WS_DISPATCH 1
 #define MOE_WS_FFN 2
 #define MOE_WS_FFN_BWD 3

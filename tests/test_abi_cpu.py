@@ -21,7 +21,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     for st in (0, -1, -2, -3, -4, -5):
         assert len(L.status_string(st)) >= 2
 
@@ -73,6 +73,19 @@ def test_null_pointers_rejected():
         st = L.lib().moe_expert_ffn(ctypes.byref(cfg), 1, None, 1, ctypes.byref(w), 1, 1, 1, 1, 1 << 40, 0, None)
         L._check("moe_expert_ffn", st)
     assert e.value.status == L.MOE_ERR_NULL                                # shared weights missing
+
+
+def test_route_without_scores_needs_workspace():
+    """moe_route may leave out the [T, E] affinities; it then needs its workspace (room for
+    them), and an input of affinities (MOE_SCORES_IN) cannot be NULL."""
+    cfg = _cfg()
+    need = L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE)
+    assert need == MID.T * MID.E * 4
+    fn = L.lib().moe_route
+    assert fn(ctypes.byref(cfg), 1, 1, None, 1, None, 0, 1, 1, None, 0, None) == L.MOE_ERR_WORKSPACE
+    assert fn(ctypes.byref(cfg), 1, 1, None, 1, None, 0, 1, 1, 1, need - 1, None) == L.MOE_ERR_WORKSPACE
+    assert fn(ctypes.byref(cfg), None, None, None, 1, None, L.MOE_SCORES_IN, 1, 1, 1, need, None) == L.MOE_ERR_NULL
+    assert L.moe_workspace_bytes(_cfg(T=0), L.MOE_WS_ROUTE) == 256
 
 
 def test_workspace_too_small_rejected():
