@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4, -5
+MOE_ERR_SCRATCH = -6
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SCORES_IN = 1
 MOE_FFN_ALL, MOE_FFN_GATE_UP, MOE_FFN_DOWN = 0, 1, 2
@@ -65,6 +66,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "moe_route": [cfgp, vp, vp, vp, vp, vp, u32, vp, vp, vp, sz, vp],
             "moe_dispatch": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "moe_dispatch_noalloc": [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
             "moe_expert_ffn": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, vp, sz,
                                ctypes.c_int, vp],
             "moe_expert_ffn_gather": [cfgp, vp, vp, vp, ctypes.POINTER(MoeExpertWeights), vp, vp, vp, sz,
@@ -158,6 +160,12 @@ def moe_dispatch(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_sc
     _check("moe_dispatch", lib().moe_dispatch(ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts), _p(offsets),
                                               _p(perm), _p(inv), _p(x_perm), _p(x_perm_scale), _p(ws),
                                               _nbytes(ws), _s(stream)))
+
+
+def moe_dispatch_noalloc(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale, stream=None):
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        ctypes.byref(cfg), _p(topk_idx), _p(x), _p(counts), _p(offsets), _p(perm), _p(inv), _p(x_perm),
+        _p(x_perm_scale), _s(stream)))
 
 
 def expert_weights(w_gate_up, w_down, ws_gate_up=None, ws_down=None, w_gate_up_scale=None,

@@ -80,6 +80,7 @@ extern "C" const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "dtype combination or option not supported";
     case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_SCRATCH: return "sizes exceed the fixed scratch of a no-allocation entry point";
   }
   return "unknown status";
 }

@@ -12,6 +12,8 @@
 // pair learns how many earlier pairs of its segment share its expert, and one
 // leader lane per expert updates the segment's LDS counter.  A column scan over
 // segments turns the per-segment counts into stable destinations.
+#include <mutex>
+
 #include "common.h"
 #include "ffn_layout.h"
 #include "kernels.h"
@@ -318,22 +320,13 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(const bf16_t* __re
   if (threadIdx.x == 0) scales[(mat * nbr + br) * nbc + bc] = sc;
 }
 
-}  // namespace moe
-
-using namespace moe;
-
-extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
-                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
-                                   void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
-                                   void* stream) {
-  moe_status st = validate_cfg(cfg);
-  if (st != MOE_OK) return st;
+// The kernels of moe_dispatch, with the per-segment counts in `segc`
+// (dispatch_segments(cfg) * E int32, no contents required).  Arguments checked.
+static moe_status dispatch_launch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                                  int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm, float* x_perm_scale,
+                                  int32_t* segc, hipStream_t s) {
+  moe_status st;
   const bool fp8 = cfg->wgt == MOE_FP8_E4M3;
-  // x_perm == nullptr: indices only (the expert FFN gathers the rows itself)
-  if (!topk_idx || !counts || !offsets || !perm || !inv || !ws) return MOE_ERR_NULL;
-  if (x_perm && (!x || (fp8 && !x_perm_scale))) return MOE_ERR_NULL;
-  if (ws_bytes < dispatch_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
-  hipStream_t s = as_stream(stream);
   const int64_t N = pairs(cfg);
   const int64_t nseg = dispatch_segments(cfg);
   const int E = cfg->E;
@@ -341,7 +334,6 @@ extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, 
   while ((1 << nbits) < E) ++nbits;
   int Ep2 = 1;
   while (Ep2 < E) Ep2 <<= 1;
-  int32_t* segc = static_cast<int32_t*>(ws);
   const unsigned blocks = (unsigned)((nseg + 3) / 4);
   if (nseg > 0) {
     hipLaunchKernelGGL(count_kernel, dim3(blocks), dim3(256), 4 * E * sizeof(int32_t), s, topk_idx, N,
@@ -367,6 +359,74 @@ extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, 
                        cfg->T, cfg->k, nchunk, (uint4*)x_perm);
   }
   return launch_status();
+}
+
+static moe_status dispatch_check(const moe_cfg* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, void* x_perm, float* x_perm_scale) {
+  moe_status st = validate_cfg(cfg);
+  if (st != MOE_OK) return st;
+  const bool fp8 = cfg->wgt == MOE_FP8_E4M3;
+  // x_perm == nullptr: indices only (the expert FFN gathers the rows itself)
+  if (!topk_idx || !counts || !offsets || !perm || !inv) return MOE_ERR_NULL;
+  if (x_perm && (!x || (fp8 && !x_perm_scale))) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                                   int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                   void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  moe_status st = dispatch_check(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale);
+  if (st != MOE_OK) return st;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < dispatch_ws_bytes(cfg)) return MOE_ERR_WORKSPACE;
+  return dispatch_launch(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale,
+                         static_cast<int32_t*>(ws), as_stream(stream));
+}
+
+// ------------------------------------------------ dispatch without a workspace
+// The per-segment counts live in a fixed array of device memory that belongs
+// to the library (one copy per GPU, held until the process ends).  Host code
+// never passes the array's name to a kernel: on the host it only stands for
+// the symbol; the array's device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+namespace moe {
+namespace {
+__device__ __align__(256) int32_t scratch[kDispatchScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+int32_t* scratch_ptr[kMaxDevices];   // device address of `scratch` per device, once known
+
+moe_status scratch_on_current_device(int32_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_LAUNCH;
+    scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                           void* x_perm, float* x_perm_scale, void* stream) {
+  moe_status st = dispatch_check(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale);
+  if (st != MOE_OK) return st;
+  if ((size_t)dispatch_segments(cfg) * cfg->E * sizeof(int32_t) > kDispatchScratchBytes) return MOE_ERR_SCRATCH;
+  int32_t* segc = nullptr;
+  if ((st = scratch_on_current_device(&segc)) != MOE_OK) return st;
+  return dispatch_launch(cfg, topk_idx, x, counts, offsets, perm, inv, x_perm, x_perm_scale, segc,
+                         as_stream(stream));
 }
 
 extern "C" moe_status moe_quantize_fp8(const void* src_bf16, int32_t n_mat, int32_t rows, int32_t cols,

@@ -12,6 +12,10 @@ inline int64_t dispatch_segments(const moe_cfg* c) {
   return (pairs(c) + kSegPairs - 1) / kSegPairs;
 }
 
+// The fixed scratch of moe_dispatch_noalloc: per-segment counts of at most
+// this many bytes (E = 256: up to 4096 segments, 4M (token, slot) pairs).
+constexpr size_t kDispatchScratchBytes = (size_t)4 << 20;
+
 inline size_t dispatch_ws_bytes(const moe_cfg* c) {
   size_t b = (size_t)dispatch_segments(c) * c->E * sizeof(int32_t);
   return align_up(b < 256 ? 256 : b, 256);

@@ -43,7 +43,8 @@ typedef enum {
   MOE_ERR_SHAPE = -2,       /* sizes inconsistent or outside the supported range */
   MOE_ERR_UNSUPPORTED = -3, /* dtype combination or option not implemented */
   MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_bytes() */
-  MOE_ERR_LAUNCH = -5       /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_LAUNCH = -5,      /* a kernel launch failed (hipGetLastError) */
+  MOE_ERR_SCRATCH = -6      /* sizes exceed the fixed scratch of a no-allocation entry point */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
@@ -149,6 +150,27 @@ moe_status moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, const void*
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
                         void* x_perm, float* x_perm_scale, void* ws, size_t ws_bytes,
                         void* stream);
+
+/*
+ * moe_dispatch_noalloc - moe_dispatch without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, results
+ * and errors as moe_dispatch, bit for bit.
+ *
+ * Its per-segment counts live in a fixed 4 MiB array of device memory owned by
+ * the library: one copy per GPU, held until the process ends; the first call
+ * on a device looks up that copy's address (hipGetSymbolAddress).  Nothing is
+ * allocated, by the library or anything it calls.  Limit: ceil(T*k / 1024) * E
+ * * 4 bytes <= 4 MiB (E = 256: T*k up to 4M pairs), else MOE_ERR_SCRATCH
+ * (checked before any device call).  Every call on a GPU shares that GPU's
+ * array and nothing in it needs to start at zero; calls that overlap on one
+ * GPU (different streams, or threads without ordering) race and give
+ * undefined results.  MOE_ERR_LAUNCH also when the array's address cannot be
+ * obtained on the current device.
+ */
+moe_status moe_dispatch_noalloc(const moe_cfg* cfg, const int32_t* topk_idx, const void* x,
+                                int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv,
+                                void* x_perm, float* x_perm_scale, void* stream);
 
 /* Expert weights.  Scales are only read when wgt == FP8_E4M3 (then the weight
  * tensors hold E4M3 bytes, one fp32 scale per 128 x 128 block). */

@@ -22,7 +22,7 @@ def test_exports_every_header_function(lib):
 
 def test_version_and_status_strings(lib):
     assert L.moe_abi_version() == 5
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         assert len(L.status_string(st)) >= 2
 
 
@@ -86,6 +86,15 @@ def test_route_without_scores_needs_workspace():
     assert fn(ctypes.byref(cfg), 1, 1, None, 1, None, 0, 1, 1, 1, need - 1, None) == L.MOE_ERR_WORKSPACE
     assert fn(ctypes.byref(cfg), None, None, None, 1, None, L.MOE_SCORES_IN, 1, 1, 1, need, None) == L.MOE_ERR_NULL
     assert L.moe_workspace_bytes(_cfg(T=0), L.MOE_WS_ROUTE) == 256
+
+
+def test_dispatch_noalloc_scratch_limit():
+    """The dispatch without a workspace refuses, before any device call, sizes whose
+    per-segment counts exceed its fixed 4 MiB scratch (ceil(T*k/1024) * E * 4 bytes)."""
+    fn = L.lib().moe_dispatch_noalloc
+    big = L.make_cfg(524416, 128, 256, 8, 4, 8, 0, 128, 2, 1.0, "bf16", "bf16")   # 4097 segments
+    assert fn(ctypes.byref(big), 1, None, 1, 1, 1, 1, None, None, None) == L.MOE_ERR_SCRATCH
+    assert fn(ctypes.byref(_cfg()), None, None, 1, 1, 1, 1, None, None, None) == L.MOE_ERR_NULL
 
 
 def test_workspace_too_small_rejected():
