@@ -63,6 +63,13 @@ struct GemmParams {
   int T, H, E, S, I, k;
 };
 
+// bf16 elements of LDS a tile's ring needs: STAGES slices of (BM + BN) x BK,
+// plus a spare 1 KB when the slice's loads do not divide evenly over the NW
+// wavefronts (the short ones issue a dropped load there).
+constexpr int ring_elems(int BM, int BN, int BK, int STAGES, int NW) {
+  return STAGES * (BM + BN) * BK + (((BM + BN) * (BK / 8) / 64) % NW ? 512 : 0);
+}
+
 // Tile of (WM*MI*32) token rows x (WN*NI*32) weight rows; wave (wm, wn) owns
 // MI x NI MFMA 32x32 blocks.  K advances BK columns per slice through a ring of
 // STAGES LDS stages filled by direct-to-LDS loads.  `lds` holds STAGES stages.
@@ -75,12 +82,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   constexpr int BM = WM * MI * 32;
   constexpr int BN = WN * NI * 32;
   constexpr int CPR = BK / 8;             // 16-byte chunks per LDS row
-  constexpr int A_CH = BM * CPR / NT;     // direct-to-LDS loads per thread per slice
-  constexpr int B_CH = BN * CPR / NT;
-  constexpr int PER = A_CH + B_CH;
+  constexpr int NA = BM * CPR / 64;       // direct-to-LDS instructions of a slice: A rows
+  constexpr int NB = BN * CPR / 64;       //   weight rows
+  constexpr int PER = (NA + NB + NW - 1) / NW;   // per wave (a short wave's last one is a dropped dummy)
   constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
-  static_assert(BM * CPR % NT == 0 && BN * CPR % NT == 0, "whole loads per thread");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  static_assert(BM * CPR % 64 == 0 && BN * CPR % 64 == 0, "whole 64-lane instructions");
+  // (the wavefront index is uniform: kept in an SGPR, so are the load slots below)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const bool shared = !is_router(MODE) && seg == p.E;
   // Routed gate/up rows gathered straight from x: row row0 + r of the
@@ -122,34 +130,48 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   }
 
   // Direct-to-LDS loads: one buffer_load_dwordx4 ... lds fills 1 KB of LDS,
-  // lane l at +16*l.  Instruction i of wave w covers chunks [(i*NW + w)*64, +64)
-  // of the A (or B) region; the lane loads the logical chunk that the XOR
-  // swizzle places at its physical position.  Token rows past the tile's valid
-  // rows get an offset outside the A descriptor, so the hardware drops them
-  // without a memory request (their LDS rows feed only outputs that are never
-  // stored); weight rows past the valid columns are clamped.
-  int a_off[A_CH], b_off[B_CH];
+  // lane l at +16*l.  The slice's instructions are numbered A first (NA of
+  // them), then B (NB); instruction i of wave w is number i*NW + w and covers
+  // chunks [64 n, 64 n + 64) of its region; the lane loads the logical chunk
+  // that the XOR swizzle places at its physical position.  Token rows past the
+  // tile's valid rows get an offset outside the A descriptor, so the hardware
+  // drops them without a memory request (their LDS rows feed only outputs that
+  // are never stored); weight rows past the valid columns are clamped.  When
+  // NA + NB is not a multiple of NW, the waves left short issue one more load
+  // with such an out-of-range offset into a spare 1 KB of LDS past the ring,
+  // so that every wave has PER loads per slice to wait on.
+  int ld_off[PER], ld_pos[PER];
+  bool ld_a[PER];
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
-    int src = r < rows ? r : a_rows + 1;
-    if constexpr (is_gate_up(MODE))
-      if (gather && r < rows) src = p.perm[row0 + r] / p.k;
-    a_off[i] = src * lda + swz<CPR>(r, pc) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int q = (i * NW + wave) * 64 + lane, r = q / CPR, pc = q % CPR;
-    int wrow;
-    if constexpr (is_gate_up(MODE)) {
-      // rows [0, BN/2) gate, [BN/2, BN) up, of h columns nt*BN/2 + j
-      const bool up = r >= BN / 2;
-      const int c = min(nt * (BN / 2) + (up ? r - BN / 2 : r), ncols - 1);
-      wrow = (c / p.I) * 2 * p.I + (up ? p.I : 0) + c % p.I;
+  for (int i = 0; i < PER; ++i) {
+    const int n = i * NW + wave;          // wave-uniform
+    if (n < NA) {
+      const int q = n * 64 + lane, r = q / CPR, pc = q % CPR;
+      int src = r < rows ? r : a_rows + 1;
+      if constexpr (is_gate_up(MODE))
+        if (gather && r < rows) src = p.perm[row0 + r] / p.k;
+      ld_off[i] = src * lda + swz<CPR>(r, pc) * 8;
+      ld_pos[i] = n * 512;
+      ld_a[i] = true;
+    } else if (n < NA + NB) {
+      const int q = (n - NA) * 64 + lane, r = q / CPR, pc = q % CPR;
+      int wrow;
+      if constexpr (is_gate_up(MODE)) {
+        // rows [0, BN/2) gate, [BN/2, BN) up, of h columns nt*BN/2 + j
+        const bool up = r >= BN / 2;
+        const int c = min(nt * (BN / 2) + (up ? r - BN / 2 : r), ncols - 1);
+        wrow = (c / p.I) * 2 * p.I + (up ? p.I : 0) + c % p.I;
+      } else {
+        wrow = min(nt * BN + r, ncols - 1);
+      }
+      ld_off[i] = wrow * ldw + swz<CPR>(r, pc) * 8;
+      ld_pos[i] = BM * BK + (n - NA) * 512;
+      ld_a[i] = false;
     } else {
-      wrow = min(nt * BN + r, ncols - 1);
+      ld_off[i] = (a_rows + 1) * lda;     // past the A descriptor: dropped
+      ld_pos[i] = -1;                      // the spare LDS past the ring
+      ld_a[i] = true;
     }
-    b_off[i] = wrow * ldw + swz<CPR>(r, pc) * 8;
   }
   // Buffer descriptors over this tile's A rows and this segment's weights: the
   // per-lane part of every address is a 32-bit byte offset, the K advance an
@@ -162,22 +184,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A, a_rows * lda * 2);
   const __amdgpu_buffer_rsrc_t rsrc_w = make_rsrc(W, w_bytes);
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) a_off[i] *= 2;
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) b_off[i] *= 2;
+  for (int i = 0; i < PER; ++i) ld_off[i] *= 2;
   typedef __attribute__((address_space(3))) void lds_void_t;
 #define MOE_ISSUE(stage_, k0_)                                                                       \
   {                                                                                                  \
     const int k0v = (k0_);                                                                           \
     const int wk = MODE == kDown ? (int)((k0v / p.I) * seg_kstride) + (k0v % p.I) : k0v;             \
     bf16_t* sb = lds + (stage_) * STAGE;                                                             \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                                 \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)(sb + (i * NW + wave) * 512), 16, \
-                                                 a_off[i], k0v * 2, 0, 0);                           \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w,                                             \
-                                                 (lds_void_t*)(sb + BM * BK + (i * NW + wave) * 512), \
-                                                 16, b_off[i], wk * 2, 0, 0);                        \
+    _Pragma("unroll") for (int i = 0; i < PER; ++i) {                                                \
+      bf16_t* dst = ld_pos[i] < 0 ? lds + STAGES * STAGE : sb + ld_pos[i];                           \
+      if (ld_a[i])                                                                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_a, (lds_void_t*)dst, 16, ld_off[i], k0v * 2, 0, 0); \
+      else                                                                                           \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_w, (lds_void_t*)dst, 16, ld_off[i], wk * 2, 0, 0); \
+    }                                                                                                \
   }
 
   f32x16_t acc[MI][NI];
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   static_assert(MI_ALT >= 0 && MI_ALT < MI, "the alternative body has fewer row blocks");
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = WM * MI * 32;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * (BM + WN * NI * 32) * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t lds[ring_elems(BM, WN * NI * 32, BK, STAGES, WM * WN)];
   // ------------------------------------------------------------ which tile
   int seg = 0, row0, rows, nt;
   if constexpr (MODE == kRouter) {
@@ -449,7 +469,7 @@ template <int EPL, int TOPR, int WM, int WN, int MI, int NI, int BK, int STAGES>
 __global__ __launch_bounds__(64 * WM * WN) void router_topk_kernel(GemmParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = WM * MI * 32, BN = WN * NI * 32;
-  constexpr int RING = STAGES * (BM + BN) * BK, SCO = 2 * BM * BN;   // in bf16 elements
+  constexpr int RING = ring_elems(BM, BN, BK, STAGES, WM * WN), SCO = 2 * BM * BN;   // in bf16 elements
   constexpr int TPP = 64 * WM * WN / 16;                            // tokens per pass
   static_assert(16 * EPL <= BN && BM % TPP == 0, "a tile holds every expert; whole passes");
   __shared__ __attribute__((aligned(16))) bf16_t lds[RING > SCO ? RING : SCO];
