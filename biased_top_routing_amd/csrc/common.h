@@ -46,38 +46,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
-// OCP E4M3FN encoder: nearest representable value, ties to the even code,
-// magnitudes above 448 saturate to 448.  Written from the format definition
-// (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, exponent field 0
-// holds the subnormals m/8 * 2^-6).
-__device__ __forceinline__ fp8_t f32_to_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return (fp8_t)(sign | 0x7Eu);        // |v| >= 448
-  int32_t e = (int32_t)(a >> 23) - 127;                      // unbiased exponent
-  uint32_t code;
-  if (e >= -6) {
-    // normal range of E4M3: keep 3 mantissa bits, round the 20 dropped bits
-    uint32_t m = a & 0x7FFFFFu;
-    uint32_t keep = m >> 20;
-    uint32_t rest = m & 0xFFFFFu;
-    uint32_t c = ((uint32_t)(e + 7) << 3) | keep;
-    if (rest > 0x80000u || (rest == 0x80000u && (c & 1u))) c += 1;   // may carry into the exponent
-    code = c;
-  } else {
-    // subnormal range: value = n * 2^-9 with n in [0, 8]; round |v| * 2^9
-    // (exact: a power-of-two scale of a value below 2^-6) to an integer,
-    // ties to even; n == 8 is the smallest normal code 0x08.
-    float scaled = __uint_as_float(a) * 512.0f;
-    float fl = floorf(scaled);
-    float frac = scaled - fl;
-    uint32_t n = (uint32_t)fl;
-    if (frac > 0.5f || (frac == 0.5f && (n & 1u))) n += 1;
-    code = n;
-  }
-  if (code > 0x7Eu) code = 0x7Eu;
-  return (fp8_t)(sign | code);
+// fl32(v / sc) for a scale sc with y = fl32(1 / sc): the product q0 = v * y is
+// within one ulp of the quotient, its remainder v - q0 * sc is exact by FMA, and
+// one correction step q0 + remainder * y then rounds to the correctly rounded
+// quotient (Markstein's theorem) as long as neither the remainder nor the
+// quotient underflows; for |v| or |q0| below 2^-100 the IEEE division is taken.
+__device__ __forceinline__ float div_by_scale(float v, float sc, float y) {
+  const float q0 = v * y;
+  const float r = fmaf(-q0, sc, v);
+  float q = fmaf(r, y, q0);
+  if (fminf(fabsf(v), fabsf(q0)) < 0x1p-100f) q = __fdiv_rn(v, sc);
+  return q;
+}
+
+// Four values as OCP E4M3FN codes (bytes 0..3 = a, b, c, d) by the hardware
+// conversion: nearest, ties to the even code.  For every fp32 |v| <= 448 (all the
+// quantisers here produce: |v| <= amax = 448 sc) it equals an encoder written from
+// the format definition (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// subnormals m/8 * 2^-6), checked over every such fp32 value.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float e4m3_to_f32(fp8_t c) {

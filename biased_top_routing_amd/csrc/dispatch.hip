@@ -197,13 +197,12 @@ __device__ __forceinline__ uint2 quant_chunk_1x128(uint4 raw, float* sc_out) {
 #pragma unroll
   for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
-  uint32_t lo = 0, hi = 0;
+  const float y = __fdiv_rn(1.0f, sc);
+  float q[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[i], sc)) << (8 * i);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[4 + i], sc)) << (8 * i);
+  for (int i = 0; i < 8; ++i) q[i] = div_by_scale(v[i], sc, y);   // fl32(v / sc)
   *sc_out = sc;
-  return make_uint2(lo, hi);
+  return make_uint2(e4m3x4(q[0], q[1], q[2], q[3]), e4m3x4(q[4], q[5], q[6], q[7]));
 }
 
 // fp8 dispatch: quantise the token's bf16 row per 1x128 tile once, then store
@@ -306,16 +305,16 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(const bf16_t* __re
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  const float y = __fdiv_rn(1.0f, sc);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = threadIdx.x + 256 * i;
     const int r = q >> 4, cc = q & 15;
-    uint32_t lo = 0, hi = 0;
+    float t[8];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[8 * i + h], sc)) << (8 * h);
-#pragma unroll
-    for (int h = 0; h < 4; ++h) hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(v[8 * i + 4 + h], sc)) << (8 * h);
-    *reinterpret_cast<uint2*>(d + (int64_t)(br * 128 + r) * cols + bc * 128 + cc * 8) = make_uint2(lo, hi);
+    for (int h = 0; h < 8; ++h) t[h] = div_by_scale(v[8 * i + h], sc, y);   // fl32(v / sc)
+    *reinterpret_cast<uint2*>(d + (int64_t)(br * 128 + r) * cols + bc * 128 + cc * 8) =
+        make_uint2(e4m3x4(t[0], t[1], t[2], t[3]), e4m3x4(t[4], t[5], t[6], t[7]));
   }
   if (threadIdx.x == 0) scales[(mat * nbr + br) * nbc + bc] = sc;
 }

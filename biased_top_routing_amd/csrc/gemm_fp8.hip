@@ -368,7 +368,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #pragma unroll
         for (int b = 0; b < HALF; ++b) {
           const float gv = acc[mi][b][r], uv = acc[mi][b + HALF][r];
-          const float h = gv / (1.0f + expf(-gv)) * uv;
+          const float h = gv / (1.0f + __expf(-gv)) * uv;
           acc[mi][b][r] = h;     // h replaces the gate accumulator
           m = fmaxf(m, fabsf(h));
         }
@@ -390,11 +390,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #pragma unroll
         for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[i * WN + w2]);
         const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
+        const float y = __fdiv_rn(1.0f, sc);
         const int64_t row = row0 + i;
 #pragma unroll
         for (int b = 0; b < HALF; ++b) {
           const int col = nt * 128 + wn * HALF * 16 + b * 16 + l16;
-          if (col < ncols) out[row * ncols + col] = f32_to_e4m3(__fdiv_rn(acc[mi][b][r], sc));
+          if (col < ncols) out[row * ncols + col] = (fp8_t)e4m3x4(div_by_scale(acc[mi][b][r], sc, y), 0.f, 0.f, 0.f);
         }
         if (wn == 0 && l16 == 0) out_s[row * ntile + nt] = sc;
       }
