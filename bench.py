@@ -50,6 +50,13 @@ def parse():
     ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
                     help="gather: dispatch writes the indices and the gate/up GEMM reads its rows from x "
                          "through perm; copy: dispatch also writes x_perm and the GEMM reads that")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="diagnostic: one batch's expert GEMMs against another batch's dispatch (row copy) + "
+                         "combine, one after the other and on two streams (micro-batch overlap); prints its JSON")
+    ap.add_argument("--gemm-probe", choices=("random", "zero"), default=None,
+                    help="diagnostic: time the grouped gate/up and down GEMMs alone with expert weights drawn on the "
+                         "GPU (N(0, sigma), or all zero: the same instructions on data that switches few bits), "
+                         "plus a dense hipBLASLt GEMM of the gate/up shape; prints its JSON")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this size 3 times (a plain copy kernel of known "
                          "size, for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -311,6 +318,176 @@ def train_extra(c, w, steps, warmup, alpha=1e-3, seq_len=4096):
     return out
 
 
+def two_stream(c, w, reps=5):
+    """Micro-batch overlap on one GPU: batch A's gate/up (then down) GEMM on one stream and
+    batch B's memory-bound stages (dispatch with the row copy, then combine) on a second
+    stream, against the same kernels one after the other.  Both batches share the weights."""
+    import copy
+
+    import numpy as np
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    from biased_top_routing_amd.runner import MoeLayerGPU
+    from workloads.inputs import make_x
+
+    la = MoeLayerGPU(c, w, gather=False, keep_scores=False)
+    lb = copy.copy(la)
+    lb.alloc(c.T)
+    xa, xb = to_dev(make_x(c, 0)), to_dev(make_x(c, 1))
+    bias = torch.from_numpy(w.bias0.copy()).cuda()
+    for lay, x in ((la, xa), (lb, xb)):
+        lay.forward(x, bias)
+    torch.cuda.synchronize()
+    s1 = torch.cuda.current_stream()
+    s2 = torch.cuda.Stream()
+    out = {}
+    for gemm, phase in (("gate_up", L.MOE_FFN_GATE_UP), ("down", L.MOE_FFN_DOWN)):
+        def gemm_a():
+            la.expert_ffn(xa, phase)
+
+        def mem_b():
+            lb.dispatch(xb)
+            lb.combine()
+
+        def timed(fn):
+            ts = []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return float(np.median(ts))
+
+        t_gemm = timed(gemm_a)
+        t_mem = timed(mem_b)
+
+        def sequential():
+            gemm_a()
+            mem_b()
+
+        def concurrent():
+            s2.wait_stream(s1)
+            gemm_a()
+            with torch.cuda.stream(s2):
+                mem_b()
+            s1.wait_stream(s2)
+
+        out[gemm] = {"gemm_ms": round(t_gemm, 4), "dispatch_combine_ms": round(t_mem, 4),
+                     "sequential_ms": round(timed(sequential), 4), "two_streams_ms": round(timed(concurrent), 4)}
+        log(f"two streams, {gemm}: {out[gemm]}")
+    return {"workload": c.name, "T": c.T, "reps": reps, "stages": out,
+            "note": "batch A's expert GEMM on the default stream, batch B's dispatch (row copy) + combine on a "
+                    "second stream of the same priority; median of the repetitions"}
+
+
+def gemm_probe(c, w, kind, reps=8):
+    """The grouped expert GEMMs alone at the workload's routing (the real router on
+    make_x(c, 0)), with expert weights drawn on the GPU: N(0, sigma) ("random") or all
+    zero ("zero", the same instruction stream on operands that switch few bits, which
+    shows how far the chip's power limit holds the clock down).  Also a dense
+    hipBLASLt GEMM (torch.mm) of the gate/up shape for every token with its weights as
+    [out, in] and as [in, out]."""
+    import numpy as np
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    from workloads.inputs import make_x
+
+    dev = "cuda"
+
+    def draw(n, rows, cols):
+        t = torch.empty((n, rows, cols), dtype=torch.bfloat16, device=dev)
+        for i in range(n):
+            if kind == "zero":
+                t[i].zero_()
+            else:
+                t[i].normal_(0.0, c.sigma)
+        return t
+
+    wgu, wd = draw(c.E, 2 * c.I, c.H), draw(c.E, c.H, c.I)
+    sgu, sd = draw(c.S, 2 * c.I, c.H), draw(c.S, c.H, c.I)
+    if c.wgt == "fp8_e4m3":
+        q = []
+        for t in (wgu, wd, sgu, sd):
+            n, r, k = t.shape
+            codes = torch.empty((n, r, k), dtype=torch.uint8, device=dev)
+            sc = torch.empty((n, r // 128, k // 128), dtype=torch.float32, device=dev)
+            if n:
+                L.moe_quantize_fp8(t, n, r, k, 128, codes, sc)
+            q.append((codes, sc))
+        W = L.expert_weights(q[0][0], q[1][0], q[2][0], q[3][0], q[0][1], q[1][1], q[2][1], q[3][1])
+    else:
+        W = L.expert_weights(wgu, wd, sgu, sd)
+    cfg = L.cfg_from(c)
+    x = to_dev(make_x(c, 0))
+    wr = to_dev(w.w_router)
+    off = torch.from_numpy(w.logit_offset).to(dev) if w.logit_offset is not None else None
+    bias = torch.from_numpy(w.bias0.copy()).to(dev)
+    idx = torch.empty((c.T, c.k), dtype=torch.int32, device=dev)
+    gw = torch.empty((c.T, c.k), dtype=torch.float32, device=dev)
+    L.moe_route(cfg, x, wr, off, bias, torch.empty((c.T, c.E), device=dev), 0, idx, gw)
+    counts = torch.empty(c.E, dtype=torch.int32, device=dev)
+    offs = torch.empty(c.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(c.T * c.k, dtype=torch.int32, device=dev)
+    inv = torch.empty((c.T, c.k), dtype=torch.int32, device=dev)
+    wsd = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_DISPATCH), dtype=torch.uint8, device=dev)
+    L.moe_dispatch(cfg, idx, None, counts, offs, perm, inv, None, None, wsd)
+    yp = torch.empty((c.T * c.k, c.H), dtype=torch.bfloat16, device=dev)
+    ys = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=dev)
+    wsf = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_FFN), dtype=torch.uint8, device=dev)
+
+    def run(ph):
+        L.moe_expert_ffn_gather(cfg, x, perm, offs, W, yp, ys, wsf, ph)
+
+    out = {"workload": c.name, "weights": kind, "reps": reps}
+    for name, ph, flops in (("gate_up", L.MOE_FFN_GATE_UP, c.gate_up_flops()), ("down", L.MOE_FFN_DOWN, c.down_flops())):
+        for _ in range(3):
+            run(L.MOE_FFN_GATE_UP)
+            run(ph)
+        ts = []
+        for _ in range(reps):
+            if ph == L.MOE_FFN_DOWN:
+                run(L.MOE_FFN_GATE_UP)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(ph)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        out[name] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+        log(f"gemm probe ({kind}) {name}: {out[name]}")
+    M, N, K = c.T * (c.k + c.S), 2 * c.I, c.H
+    M = min(M, 32768)
+    a = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    b_nk = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    b_kn = torch.empty((K, N), dtype=torch.bfloat16, device=dev)
+    for t, sd_ in ((a, 1.0), (b_nk, c.sigma), (b_kn, c.sigma)):
+        if kind == "zero":
+            t.zero_()
+        else:
+            t.normal_(0.0, sd_)
+    for name, f in (("hipblaslt_x_WT", lambda: torch.mm(a, b_nk.t())), ("hipblaslt_x_W", lambda: torch.mm(a, b_kn))):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"M": M, "N": N, "K": K, "ms": round(ms, 4), "tflops": round(2 * M * N * K / ms / 1e9, 1)}
+        log(f"gemm probe ({kind}) {name}: {out[name]}")
+    return out
+
+
 def balance_trajectory(layer, c, w, steps):
     """Per-step expert load over `steps` consecutive batches of the layer with the bias
     update between them.  Batch i's x is make_x(c, i) from the shared seeded generator
@@ -455,6 +632,10 @@ def main():
     L.lib()     # fails loudly without the built library
     c = CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.gemm_probe:
+        from workloads.inputs import make_router
+        print(json.dumps(gemm_probe(c, make_router(c), args.gemm_probe)), flush=True)
+        return
     log(f"workload {c.name}: generating seeded inputs")
     t0 = time.perf_counter()
     w = make_weights(c)
@@ -462,6 +643,9 @@ def main():
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s; uploading")
     if args.train_only:
         print(json.dumps(train_extra(c, w, args.steps, args.warmup)), flush=True)
+        return
+    if args.two_stream:
+        print(json.dumps(two_stream(c, w, max(args.steps, 3))), flush=True)
         return
     gather = args.dispatch == "gather"
     layer = MoeLayerGPU(c, w, gather=gather, keep_scores=False)

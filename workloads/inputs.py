@@ -143,6 +143,14 @@ class LayerWeights:
     bias0: np.ndarray           # [E] float32
 
 
+def make_router(cfg: MoeConfig) -> LayerWeights:
+    """The router part of make_weights (router weight, logit offset, initial bias; the
+    same values), with empty expert tensors: for runs that draw expert weights elsewhere."""
+    w_router = _encode(_normal(rng(cfg.seed, TAG_WR), (cfg.E, cfg.H), cfg.sigma), cfg.act)
+    empty = np.empty((0,), dtype=_store_dtype(cfg.wgt))
+    return LayerWeights(w_router, empty, empty, empty, empty, make_logit_offset(cfg), make_bias0(cfg))
+
+
 def make_weights(cfg: MoeConfig) -> LayerWeights:
     s = cfg.seed
     w_router = _encode(_normal(rng(s, TAG_WR), (cfg.E, cfg.H), cfg.sigma), cfg.act)
