@@ -8,6 +8,9 @@
 // On gfx950 one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K
 // chunk, so the promotion is: P = A_c B_c^T of the chunk from a zero
 // accumulator, then acc += P * sa[row, c] * sw[block, c] in fp32 registers.
+// The MFMA takes the weight fragment as its first operand, so a lane's four
+// results are four adjacent weight columns of one token row: they share one
+// scale product sa * sw, and the epilogue stores them as one word.
 // (The FP8 MFMA's own sum of a chunk's products is not exact for codes of a
 // wide exponent range; starting every chunk from zero keeps that error from
 // growing with K.)
@@ -95,10 +98,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int 
 }
 #endif
 
-__device__ __forceinline__ i32x8_t frag(const uint8_t* rowp, int r, int g) {
-  const i32x4v_t lo = *reinterpret_cast<const i32x4v_t*>(rowp + swz8(r, 2 * g) * 16);
-  const i32x4v_t hi = *reinterpret_cast<const i32x4v_t*>(rowp + swz8(r, 2 * g + 1) * 16);
-  return i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+// The 32 K bytes of lane group g in an LDS row: its two 16-byte chunks sit at
+// swizzled positions that depend only on the row's low four bits, so every
+// fragment a lane reads (rows l16 + 16 j) uses the same two byte offsets lo, hi.
+__device__ __forceinline__ i32x8_t frag(const uint8_t* rowp, int lo, int hi) {
+  const i32x4v_t a = *reinterpret_cast<const i32x4v_t*>(rowp + lo);
+  const i32x4v_t b = *reinterpret_cast<const i32x4v_t*>(rowp + hi);
+  return i32x8_t{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
 template <int MODE, int WM, int WN, int MI, int NI, int STAGES>
@@ -267,8 +273,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     }
     b_rd[ni] = brow + l16;
   }
-  // rows of this lane's accumulators: 4g + r inside each 16-row block
-  const int srow0 = wm * MI * 16 + 4 * g;
+  const int c_lo = swz8(l16, 2 * g) * 16, c_hi = swz8(l16, 2 * g + 1) * 16;
+  // this lane's accumulators: token row arow0 + 16 mi, weight columns 4g + r of each 16-column block
   const int wsel = MODE == kDown8 ? (wn * NI * 16) / 128 : 0;   // down: output block of this wavefront
   const bool has_rows = wm * MI * 16 < rows;
 
@@ -287,39 +293,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
       const float w1 = sw_lds[kFp8MaxKC + kt];
       i32x8_t fb[NI];
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) fb[ni] = frag(base + BM * BK + b_rd[ni] * BK, b_rd[ni], g);
+      for (int ni = 0; ni < NI; ++ni) fb[ni] = frag(base + BM * BK + b_rd[ni] * BK, c_lo, c_hi);
       // row blocks one at a time (short live ranges); the next block's operand
       // and scale reads are issued before this block's MFMAs, and the previous
       // block's chunk products are promoted (VALU) under this block's MFMAs
-      i32x8_t fa = frag(base + arow0 * BK, arow0, g);
-      f32x4_t sa4 = *reinterpret_cast<const f32x4_t*>(sa_st + srow0);
+      const uint8_t* pa = base + arow0 * BK;   // this lane's A row in block 0; block mi is 16 mi rows further
+      const float* psa = sa_st + arow0;
+      i32x8_t fa = frag(pa, c_lo, c_hi);
+      float sa = psa[0];
       f32x4_t prev[NI];
-      float p0[4], p1[4];
+      float p0 = 0.f, p1 = 0.f;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         i32x8_t fa_n;
-        f32x4_t sa_n;
+        float sa_n = 0.f;
         if (mi + 1 < MI) {
-          fa_n = frag(base + (arow0 + (mi + 1) * 16) * BK, arow0 + (mi + 1) * 16, g);
-          sa_n = *reinterpret_cast<const f32x4_t*>(sa_st + srow0 + (mi + 1) * 16);
+          fa_n = frag(pa + (mi + 1) * 16 * BK, c_lo, c_hi);
+          sa_n = psa[(mi + 1) * 16];
         }
         __builtin_amdgcn_sched_barrier(0);
-        float s0[4], s1[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          s0[r] = sa4[r] * w0;
-          s1[r] = sa4[r] * w1;
-        }
+        const float s0 = sa * w0, s1 = sa * w1;
         f32x4_t part[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          part[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[ni], z, 0, 0, 0, 0, 0, 0);
+          part[ni] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[ni], fa, z, 0, 0, 0, 0, 0, 0);
           if (mi > 0) {
-            const bool second = MODE == kGateUp8 && ni >= NI / 2;
+            const float sp = MODE == kGateUp8 && ni >= NI / 2 ? p1 : p0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mi - 1][ni][r] = fmaf(prev[ni][r], second ? p1[r] : p0[r], acc[mi - 1][ni][r]);
+            for (int r = 0; r < 4; ++r) acc[mi - 1][ni][r] = fmaf(prev[ni][r], sp, acc[mi - 1][ni][r]);
           }
         }
         // one MFMA, then the previous block's 4 promotion FMAs of that column block
@@ -333,22 +335,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) prev[ni] = part[ni];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p0[r] = s0[r];
-          p1[r] = s1[r];
-        }
+        p0 = s0;
+        p1 = s1;
         if (mi + 1 < MI) {
           fa = fa_n;
-          sa4 = sa_n;
+          sa = sa_n;
         }
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const bool second = MODE == kGateUp8 && ni >= NI / 2;
+        const float sp = MODE == kGateUp8 && ni >= NI / 2 ? p1 : p0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[MI - 1][ni][r] = fmaf(prev[ni][r], second ? p1[r] : p0[r], acc[MI - 1][ni][r]);
+        for (int r = 0; r < 4; ++r) acc[MI - 1][ni][r] = fmaf(prev[ni][r], sp, acc[MI - 1][ni][r]);
       }
     }
     cur = cur == STAGES - 1 ? 0 : cur + 1;
@@ -356,64 +354,66 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #undef MOE_ISSUE8
 
   // ------------------------------------------------------------ epilogue
-  // acc[mi][ni][r] holds C[i][j] with j = lane % 16, i = 4 * (lane / 16) + r
+  // acc[mi][ni][r] holds C[i][j] with i = arow0 + 16 mi (token row), j = 16 ni + 4 (lane / 16) + r
   if constexpr (MODE == kGateUp8) {
     constexpr int HALF = NI / 2;
     // per row: SwiGLU in registers, amax over this wavefront's HALF*16 columns
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      float m = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = 0.f;
+      for (int b = 0; b < HALF; ++b)
 #pragma unroll
-        for (int b = 0; b < HALF; ++b) {
+        for (int r = 0; r < 4; ++r) {
           const float gv = acc[mi][b][r], uv = acc[mi][b + HALF][r];
           const float h = gv / (1.0f + __expf(-gv)) * uv;
           acc[mi][b][r] = h;     // h replaces the gate accumulator
           m = fmaxf(m, fabsf(h));
         }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-        if (l16 == 0) red[(srow0 + mi * 16 + r) * WN + wn] = m;
-      }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (g == 0) red[(arow0 + mi * 16) * WN + wn] = m;
+    }
     __syncthreads();
     fp8_t* out = static_cast<fp8_t*>(shared ? p.out_shared : p.out_routed);
     float* out_s = shared ? p.out_shared_scale : p.out_routed_scale;
     const int ntile = ncols / 128;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int i = arow0 + mi * 16;
+      if (i >= rows) continue;
+      float amax = red[i * WN];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = srow0 + mi * 16 + r;
-        if (i >= rows) continue;
-        float amax = red[i * WN];
+      for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[i * WN + w2]);
+      const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
+      const float y = __fdiv_rn(1.0f, sc);
+      const int64_t row = row0 + i;
 #pragma unroll
-        for (int w2 = 1; w2 < WN; ++w2) amax = fmaxf(amax, red[i * WN + w2]);
-        const float sc = amax == 0.f ? 1.0f : __fdiv_rn(amax, 448.0f);
-        const float y = __fdiv_rn(1.0f, sc);
-        const int64_t row = row0 + i;
-#pragma unroll
-        for (int b = 0; b < HALF; ++b) {
-          const int col = nt * 128 + wn * HALF * 16 + b * 16 + l16;
-          if (col < ncols) out[row * ncols + col] = (fp8_t)e4m3x4(div_by_scale(acc[mi][b][r], sc, y), 0.f, 0.f, 0.f);
-        }
-        if (wn == 0 && l16 == 0) out_s[row * ntile + nt] = sc;
+      for (int b = 0; b < HALF; ++b) {
+        // four adjacent h columns; ncols is a multiple of 128, so all four are in range or none
+        const int col = nt * 128 + wn * HALF * 16 + b * 16 + 4 * g;
+        if (col < ncols)
+          *reinterpret_cast<uint32_t*>(out + row * ncols + col) =
+              e4m3x4(div_by_scale(acc[mi][b][0], sc, y), div_by_scale(acc[mi][b][1], sc, y),
+                     div_by_scale(acc[mi][b][2], sc, y), div_by_scale(acc[mi][b][3], sc, y));
       }
+      if (wn == 0 && g == 0) out_s[row * ntile + nt] = sc;
+    }
   } else {
     bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi) {
+      const int i = arow0 + mi * 16;
+      if (i >= rows) continue;
+      const int64_t row = row0 + i;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = srow0 + mi * 16 + r;
-        if (i >= rows) continue;
-        const int64_t row = row0 + i;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = nt * BN + wn * NI * 16 + ni * 16 + l16;
-          if (col < ncols) out[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
-        }
+      for (int ni = 0; ni < NI; ++ni) {
+        const int col = nt * BN + wn * NI * 16 + ni * 16 + 4 * g;
+        if (col < ncols)
+          *reinterpret_cast<uint2*>(out + row * ncols + col) =
+              uint2{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
       }
+    }
   }
 #endif
 }

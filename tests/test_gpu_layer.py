@@ -304,6 +304,36 @@ def test_router_gemm_tile_heights(T, E):
         assert (w_m.view(np.uint32) == outs[0][1].view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("T", [1, 255, 256, 1000])
+def test_router_fp32_with_and_without_scores(T):
+    """The fp32 path (one thread per logit, then the top-k): the call without the
+    affinities stages them in the workspace and gives the indices and gates of the call
+    that writes them, bit for bit; those affinities match the fp64 oracle and the routing
+    is the oracle's on them."""
+    c = TINY.with_(T=T)
+    w = make_weights(c)
+    xh = make_x(c)
+    say(f"fp32 router T={T}")
+    cfg = L.cfg_from(c)
+    x, wr, off, b = to_device(xh), to_device(w.w_router), to_device(w.logit_offset), dev_f32(w.bias0)
+    s = torch.full((T, c.E), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE),), 0xFF, dtype=torch.uint8, device="cuda")
+    outs = []
+    for scores in (s, None):
+        idx = torch.full((T, c.k), -1, dtype=torch.int32, device="cuda")
+        wt = torch.full((T, c.k), -1.0, dtype=torch.float32, device="cuda")
+        L.moe_route(cfg, x, wr, off, b, scores, 0, idx, wt, None if scores is not None else ws)
+        torch.cuda.synchronize()
+        outs.append((host(idx), host(wt)))
+    s_gpu = host(s)
+    assert np.abs(s_gpu - oracle.affinity(xh, w.w_router, w.logit_offset)).max() < 1e-6
+    idx_o, w_o = oracle.route(s_gpu, w.bias0, c.G, c.M, c.k, c.group_topr, c.route_scale)
+    assert (outs[0][0] == idx_o).all()
+    np.testing.assert_allclose(outs[0][1], w_o, rtol=2e-6, atol=1e-7)
+    assert (outs[1][0] == outs[0][0]).all()
+    assert (outs[1][1].view(np.uint32) == outs[0][1].view(np.uint32)).all()
+
+
 # ---------------------------------------------------------------- gate/up row tiling boundaries
 SEG_SIZES = [1, 96, 128, 129, 160, 161, 192, 256, 257, 320, 321, 384, 512, 513, 576, 640, 641, 700, 768, 769]
 
