@@ -569,6 +569,41 @@ def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
     return out
 
 
+def permute_copy(c, x, idx, iters=10):
+    """The dispatch with the row copy (counts, offsets, perm, inv and x_perm[p] =
+    x[perm[p] / k]) on the layer's routing, with a 512 MB write between launches:
+    the permute as a memory-bound stage of its own (the default path folds the copy
+    into the gate/up GEMM's loads)."""
+    import torch
+
+    from biased_top_routing_amd import _lib as L
+    cfg = L.cfg_from(c)
+    dev = "cuda"
+    counts = torch.empty(c.E, dtype=torch.int32, device=dev)
+    offs = torch.empty(c.E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(c.T * c.k, dtype=torch.int32, device=dev)
+    inv = torch.empty((c.T, c.k), dtype=torch.int32, device=dev)
+    xp = torch.empty((c.T * c.k, c.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_DISPATCH), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    L.moe_dispatch(cfg, idx, x, counts, offs, perm, inv, xp, None, ws)
+    ms = []
+    for _ in range(iters):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.moe_dispatch(cfg, idx, x, counts, offs, perm, inv, xp, None, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    t = sorted(ms)[len(ms) // 2]
+    nbytes = stage_bytes(c, gather=False)["dispatch"]
+    del xp, flush
+    torch.cuda.empty_cache()
+    return {"ms": round(t, 4), "gbs": round(nbytes / (t * 1e-3) / 1e9, 1), "bytes": nbytes,
+            "frac_of_hbm": round(nbytes / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def small_workload(name, steps, warmup, balance_steps, gather=False):
     """One of the small configurations (tiny fp32, mid bf16): per-step time, rates, and
     the max/mean load over `balance_steps` batches (fresh x from the shared generator)."""
@@ -720,6 +755,8 @@ def main():
         extras["v3_decode_bf16"] = decode_extra(layer, c, w, max(args.steps, 20), args.warmup)
         log("extra: route stage at several batch sizes (cache flushed between launches)")
         extras["route_sweep"] = route_sweep(c, w)
+        log("extra: dispatch with the row copy (the permute as a stage of its own)")
+        extras["permute_copy"] = permute_copy(c, x, layer.topk_idx)
         del layer, x
         torch.cuda.empty_cache()
         log("extra: one training step (forward + backward) at the prefill shape")

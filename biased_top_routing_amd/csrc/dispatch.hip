@@ -138,11 +138,12 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
 }
 
 // One wavefront per token: load the token's row once, store it to each of its
-// k destination rows.  16-byte chunks; CPL chunks per lane per pass.  The
-// permuted rows are written once and read later by another kernel: the
-// stores are non-temporal.
+// k destination rows.  16-byte chunks; CPL chunks per lane per pass.  Plain
+// stores: with x read from HBM (the Infinity Cache flushed before the launch)
+// non-temporal ones were 11% slower, and a training step, which reads the
+// permuted rows back, ran at the same speed with either.
 #ifndef MOE_PERMUTE_NT
-#define MOE_PERMUTE_NT 1
+#define MOE_PERMUTE_NT 0
 #endif
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
