@@ -36,6 +36,19 @@ __device__ __forceinline__ uint64_t same_expert_lanes(int e, bool valid, int nbi
   return m;
 }
 
+// The expert ids of segment `seg` held by this lane (pair lo + 64 it + lane),
+// all loaded before any is used; -1 past the last pair.
+__device__ __forceinline__ void load_segment(const int32_t* __restrict__ idx, int64_t seg, int64_t N,
+                                             int (&ev)[kSegPairs / kWave]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t lo = seg * kSegPairs;
+#pragma unroll
+  for (int it = 0; it < kSegPairs / kWave; ++it) {
+    const int64_t f = lo + it * kWave + lane;
+    ev[it] = f < N ? idx[f] : -1;
+  }
+}
+
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int64_t N,
                                                     int E, int nbits, int64_t nseg,
                                                     int32_t* __restrict__ segcounts) {
@@ -45,13 +58,12 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
   for (int e = lane; e < E; e += kWave) cnt[e] = 0;
   __syncthreads();
-  const int64_t lo = seg * kSegPairs;
-  const int64_t hi = lo + kSegPairs < N ? lo + kSegPairs : N;
-#pragma unroll 4
+  int ev[kSegPairs / kWave];
+  load_segment(idx, seg, N, ev);
+#pragma unroll
   for (int it = 0; it < kSegPairs / kWave; ++it) {
-    const int64_t f = lo + it * kWave + lane;
-    const bool valid = f < hi;
-    const int e = valid ? idx[f] : 0;
+    const bool valid = ev[it] >= 0;
+    const int e = valid ? ev[it] : 0;
     const uint64_t m = same_expert_lanes(e, valid, nbits);
     if (valid && (m & lanes_below()) == 0) cnt[e] += __popcll(m);
   }
@@ -75,18 +87,33 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ segcou
   const int64_t chunk = (nseg + P - 1) / P;
   const int64_t s0 = part * chunk;
   const int64_t s1 = s0 + chunk < nseg ? s0 + chunk : nseg;
+  // (the column is walked in batches of kScanBatch segments whose loads are all
+  // issued before any is added)
+  constexpr int kScanBatch = 16;
   int32_t acc = 0;
   if (e < E)
-    for (int64_t s = s0; s < s1; ++s) acc += segcounts[s * E + e];
+    for (int64_t b = s0; b < s1; b += kScanBatch) {
+      int32_t c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = b + i < s1 ? segcounts[(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) acc += c[i];
+    }
   part_sum[part * Ep2 + e] = acc;
   __syncthreads();
   int32_t run = 0;
   for (int p = 0; p < part; ++p) run += part_sum[p * Ep2 + e];
   if (e < E)
-    for (int64_t s = s0; s < s1; ++s) {
-      const int32_t c = segcounts[s * E + e];
-      segcounts[s * E + e] = run;
-      run += c;
+    for (int64_t b = s0; b < s1; b += kScanBatch) {
+      int32_t c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = b + i < s1 ? segcounts[(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (b + i < s1) {
+          segcounts[(b + i) * E + e] = run;
+          run += c[i];
+        }
     }
   if (part == 0) {
     int32_t total = 0;
@@ -120,12 +147,13 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
     for (int e = lane; e < E; e += kWave) cnt[e] = offsets[e] + segprefix[seg * E + e];
   __syncthreads();
   const int64_t lo = seg * kSegPairs;
-  const int64_t hi = lo + kSegPairs < N ? lo + kSegPairs : N;
-#pragma unroll 4
+  int ev[kSegPairs / kWave];
+  load_segment(idx, seg, N, ev);
+#pragma unroll
   for (int it = 0; it < kSegPairs / kWave; ++it) {
     const int64_t f = lo + it * kWave + lane;
-    const bool valid = f < hi;
-    const int e = valid ? idx[f] : 0;
+    const bool valid = ev[it] >= 0;
+    const int e = valid ? ev[it] : 0;
     const uint64_t m = same_expert_lanes(e, valid, nbits);
     const int32_t base = valid ? cnt[e] : 0;
     const int32_t pos = base + __popcll(m & lanes_below());
