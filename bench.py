@@ -569,16 +569,23 @@ def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
     return out
 
 
-def permute_copy(c, x, idx, iters=10):
+def permute_copy(c, w, x, iters=10):
     """The dispatch with the row copy (counts, offsets, perm, inv and x_perm[p] =
-    x[perm[p] / k]) on the layer's routing, with a 512 MB write between launches:
-    the permute as a memory-bound stage of its own (the default path folds the copy
-    into the gate/up GEMM's loads)."""
+    x[perm[p] / k]) on the routing of x [T, H], with a 512 MB write between
+    launches: the permute as a memory-bound stage of its own (the default path folds
+    the copy into the gate/up GEMM's loads)."""
     import torch
 
     from biased_top_routing_amd import _lib as L
     cfg = L.cfg_from(c)
     dev = "cuda"
+    if tuple(x.shape) != (c.T, c.H):
+        raise ValueError(f"permute_copy: x is {tuple(x.shape)}, the workload needs {(c.T, c.H)}")
+    idx = torch.empty((c.T, c.k), dtype=torch.int32, device=dev)
+    gw = torch.empty((c.T, c.k), dtype=torch.float32, device=dev)
+    wsr = torch.empty(L.moe_workspace_bytes(cfg, L.MOE_WS_ROUTE), dtype=torch.uint8, device=dev)
+    off = torch.from_numpy(w.logit_offset).to(dev) if w.logit_offset is not None else None
+    L.moe_route(cfg, x, to_dev(w.w_router), off, torch.from_numpy(w.bias0.copy()).to(dev), None, 0, idx, gw, wsr)
     counts = torch.empty(c.E, dtype=torch.int32, device=dev)
     offs = torch.empty(c.E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(c.T * c.k, dtype=torch.int32, device=dev)
@@ -756,7 +763,7 @@ def main():
         log("extra: route stage at several batch sizes (cache flushed between launches)")
         extras["route_sweep"] = route_sweep(c, w)
         log("extra: dispatch with the row copy (the permute as a stage of its own)")
-        extras["permute_copy"] = permute_copy(c, x, layer.topk_idx)
+        extras["permute_copy"] = permute_copy(c, w, x)
         del layer, x
         torch.cuda.empty_cache()
         log("extra: one training step (forward + backward) at the prefill shape")

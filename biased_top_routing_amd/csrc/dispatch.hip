@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   load_segment(idx, seg, N, ev);
 #pragma unroll
   for (int it = 0; it < kSegPairs / kWave; ++it) {
-    const bool valid = ev[it] >= 0;
+    const bool valid = (unsigned)ev[it] < (unsigned)E;   // (an id outside [0, E) is not counted)
     const int e = valid ? ev[it] : 0;
     const uint64_t m = same_expert_lanes(e, valid, nbits);
     if (valid && (m & lanes_below()) == 0) cnt[e] += __popcll(m);
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* __restrict__ i
 #pragma unroll
   for (int it = 0; it < kSegPairs / kWave; ++it) {
     const int64_t f = lo + it * kWave + lane;
-    const bool valid = ev[it] >= 0;
+    const bool valid = (unsigned)ev[it] < (unsigned)E;   // (an id outside [0, E) is not counted)
     const int e = valid ? ev[it] : 0;
     const uint64_t m = same_expert_lanes(e, valid, nbits);
     const int32_t base = valid ? cnt[e] : 0;

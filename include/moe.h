@@ -133,7 +133,8 @@ moe_status moe_route(const moe_cfg* cfg, const void* x, const void* w_router,
  * counted over the whole batch (qwbw.cn essay on the DeepSeek-V3 report,
  * load-balancing section).
  *
- *  topk_idx  [T, k] int32 in (values in [0, E); out-of-range values are undefined)
+ *  topk_idx  [T, k] int32 in, values in [0, E) (a pair whose value lies outside is
+ *            not counted, and perm, inv and x_perm are then undefined)
  *  x         [T, H] act dtype in
  *  counts    [E] int32 out: pairs routed to each expert
  *  offsets   [E+1] int32 out: exclusive prefix sum of counts
