@@ -127,7 +127,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   static_assert(STAGE % 16 == 0, "stage alignment");
   constexpr int SW_OFF = STAGES * STAGE;
   constexpr int RED_OFF = SW_OFF + 2 * kFp8MaxKC * 4;
-  constexpr int LDS_BYTES = RED_OFF + BM * WN * 4;
+  // down epilogue: each wavefront stages its (MI*16) x (NI*16) bf16 outputs in LDS
+  // (rows padded to STG_PITCH bytes against bank conflicts) over the finished ring
+  constexpr int STG_PITCH = NI * 16 * 2 + 16;
+  constexpr int STG_BYTES = MODE == kDown8 ? NW * MI * 16 * STG_PITCH : 0;
+  constexpr int LDS_BYTES = RED_OFF + BM * WN * 4 > STG_BYTES ? RED_OFF + BM * WN * 4 : STG_BYTES;
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   float* sw_lds = reinterpret_cast<float*>(lds + SW_OFF);
@@ -400,19 +404,31 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
       if (wn == 0 && g == 0) out_s[row * ntile + nt] = sc;
     }
   } else {
+    // A lane holds 4 adjacent columns of a row (8 bytes); the stores go out as
+    // whole 128-byte row segments instead: the wavefront's outputs pass through
+    // LDS and each lane then stores 16 bytes, 8 lanes per row.  (Stored straight
+    // from the accumulators, in 32-byte pieces per row, the down GEMM spent ~20%
+    // of its time in the epilogue.)
+    static_assert(NI * 16 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
+    __syncthreads();   // every wavefront is done with the ring
+    uint8_t* stg = lds + wave * (MI * 16 * STG_PITCH);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        *reinterpret_cast<uint2*>(stg + (mi * 16 + l16) * STG_PITCH + (ni * 16 + 4 * g) * 2) =
+            uint2{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
+    // (the wavefront reads back only what it wrote; its LDS operations complete in order)
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
     bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+    const int col = nt * BN + wn * NI * 16 + (lane & 7) * 8;   // ncols is a multiple of 128: the segment is whole or absent
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int i = arow0 + mi * 16;
-      if (i >= rows) continue;
-      const int64_t row = row0 + i;
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        const int col = nt * BN + wn * NI * 16 + ni * 16 + 4 * g;
-        if (col < ncols)
-          *reinterpret_cast<uint2*>(out + row * ncols + col) =
-              uint2{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
-      }
+    for (int it = 0; it < MI * 16 / 8; ++it) {
+      const int lr = it * 8 + (lane >> 3);
+      const int i = wm * MI * 16 + lr;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * STG_PITCH + (lane & 7) * 16);
+      if (i < rows && col < ncols) *reinterpret_cast<uint4*>(out + (row0 + i) * (int64_t)ncols + col) = v;
     }
   }
 #endif
