@@ -63,6 +63,9 @@ struct GemmParams {
   int T, H, E, S, I, k;
 };
 
+// Row pitch (bf16 elements) of the down GEMM's output staging: 64 columns + 8.
+constexpr int kDownStagePitch = 72;
+
 // bf16 elements of LDS a tile's ring needs: STAGES slices of (BM + BN) x BK,
 // plus a spare 1 KB when the slice's loads do not divide evenly over the NW
 // wavefronts (the short ones issue a dropped load there).
@@ -296,6 +299,36 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   // i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 inside the 32 x 32 block.
   // kRouterTopk reuses the LDS ring for the [BM][BN] fp32 affinities: every
   // wavefront must be done with its last slice first.
+  if constexpr (MODE == kDown) {
+    // A lane holds single values of 16 rows; the wavefront's (MI*32) x (NI*32)
+    // outputs pass through LDS (rows padded to DSP elements against bank
+    // conflicts, over the finished ring) and go out as whole 128-byte row
+    // segments, 16 bytes per lane.
+    static_assert(NI * 32 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
+    __syncthreads();   // every wavefront is done with the ring
+    bf16_t* stg = lds + wave * (MI * 32 * kDownStagePitch);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stg[(mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * kDownStagePitch + ni * 32 + lr] =
+              f32_to_bf16(acc[mi][ni][r]);
+    // (the wavefront reads back only what it wrote; its LDS operations complete in order)
+    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
+    __builtin_amdgcn_wave_barrier();
+    bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+    const int col = nt * BN + wn * NI * 32 + (lane & 7) * 8;   // H is a multiple of 64: whole segment or none
+#pragma unroll
+    for (int it = 0; it < MI * 32 / 8; ++it) {
+      const int lr2 = it * 8 + (lane >> 3);
+      const int i = wm * MI * 32 + lr2;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + lr2 * kDownStagePitch + (lane & 7) * 8);
+      if (i < rows && col < ncols) *reinterpret_cast<uint4*>(out + (row0 + i) * (int64_t)ncols + col) = v;
+    }
+    return;
+  }
   if constexpr (MODE == kRouterTopk) __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -320,13 +353,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
               ou[row * ncols + col] = f32_to_bf16(u);
             }
           }
-        }
-      } else if constexpr (MODE == kDown) {
-        bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int col = nt * BN + wn * NI * 32 + ni * 32 + lr;
-          if (col < ncols) out[row * ncols + col] = f32_to_bf16(acc[mi][ni][r]);
         }
       } else if constexpr (MODE == kRouterTopk) {
         // the tile holds every expert of its tokens (nt == 0, BN >= E)
@@ -368,7 +394,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
   static_assert(MI_ALT >= 0 && MI_ALT < MI, "the alternative body has fewer row blocks");
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int BM = WM * MI * 32;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[ring_elems(BM, WN * NI * 32, BK, STAGES, WM * WN)];
+  constexpr int RING = ring_elems(BM, WN * NI * 32, BK, STAGES, WM * WN);
+  constexpr int STG = MODE == kDown ? WM * WN * MI * 32 * kDownStagePitch : 0;   // down: output staging
+  __shared__ __attribute__((aligned(16))) bf16_t lds[RING > STG ? RING : STG];
   // ------------------------------------------------------------ which tile
   int seg = 0, row0, rows, nt;
   if constexpr (MODE == kRouter) {

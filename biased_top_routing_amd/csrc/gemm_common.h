@@ -18,6 +18,10 @@ constexpr int kVmWaitOneStage() {
   return (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 }
 
+// s_waitcnt immediate that waits for every LDS (and scalar memory) operation of
+// this wave (vmcnt and expcnt left at their maxima).
+constexpr int kLgkmWaitZero = 0xF | (0x3 << 14) | (0x7 << 4);
+
 // Word 3 of a raw buffer descriptor (32-bit data format, no swizzle).
 constexpr int kBufferWord3 = 0x00020000;
 
