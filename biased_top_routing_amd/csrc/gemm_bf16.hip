@@ -63,8 +63,10 @@ struct GemmParams {
   int T, H, E, S, I, k;
 };
 
-// Row pitch (bf16 elements) of the down GEMM's output staging: 64 columns + 8.
+// Row pitches (bf16 elements) of the output staging: down 64 columns + 8,
+// gate/up 128 h columns + 8.
 constexpr int kDownStagePitch = 72;
+constexpr int kGateUpStagePitch = 136;
 
 // bf16 elements of LDS a tile's ring needs: STAGES slices of (BM + BN) x BK,
 // plus a spare 1 KB when the slice's loads do not divide evenly over the NW
@@ -299,6 +301,37 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   // i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 inside the 32 x 32 block.
   // kRouterTopk reuses the LDS ring for the [BM][BN] fp32 affinities: every
   // wavefront must be done with its last slice first.
+  if constexpr (MODE == kGateUp) {
+    // h = silu(g) * u for the tile's BM rows x BN/2 columns, assembled in LDS over
+    // the finished ring (rows padded to kGateUpStagePitch elements) and stored as
+    // whole 256-byte row segments, 16 bytes per lane.
+    constexpr int HALF = NI / 2;
+    constexpr int HC = BN / 2;                      // h columns of the tile
+    static_assert(HC * 2 == 256 && BM * kGateUpStagePitch <= STAGES * STAGE, "h tile staging");
+    __syncthreads();   // every wavefront is done with the ring
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+#pragma unroll
+        for (int ni = 0; ni < HALF; ++ni) {
+          const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
+          lds[i * kGateUpStagePitch + wn * HALF * 32 + ni * 32 + lr] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        }
+      }
+    __syncthreads();
+    bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+    if (nt * HC < ncols) {   // ncols (I or S*I) is a multiple of 128: the tile's columns are all valid or none
+      for (int q = threadIdx.x; q < BM * (HC / 8); q += NT) {
+        const int rr = q / (HC / 8), ch = q % (HC / 8);
+        if (rr < rows)
+          *reinterpret_cast<uint4*>(out + (row0 + rr) * (int64_t)ncols + nt * HC + ch * 8) =
+              *reinterpret_cast<const uint4*>(lds + rr * kGateUpStagePitch + ch * 8);
+      }
+    }
+    return;
+  }
   if constexpr (MODE == kDown) {
     // A lane holds single values of 16 rows; the wavefront's (MI*32) x (NI*32)
     // outputs pass through LDS (rows padded to DSP elements against bank
