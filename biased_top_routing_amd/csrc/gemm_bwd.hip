@@ -99,7 +99,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
   static_assert(BM * CPK % NT == 0 && BN * CPK % NT == 0, "whole loads per thread");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "M-contiguous slices of at least 16 chunks per row");
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(16))) bf16_t lds[STAGES * STAGE];
+  // kDx: each wavefront's (MI*32) x (NI*32) outputs are staged in LDS for the
+  // epilogue (rows padded to DX_PITCH elements), over the finished ring
+  constexpr int DX_PITCH = NI * 32 + 8;
+  constexpr int LDS_ELEMS = KIND == kDx && NW * MI * 32 * DX_PITCH > STAGES * STAGE ? NW * MI * 32 * DX_PITCH
+                                                                                     : STAGES * STAGE;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int lr = lane & 31, kh = lane >> 5;
@@ -361,6 +366,33 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
 
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] = C[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  if constexpr (KIND == kDx) {
+    // dX goes out as whole 128-byte row segments, 16 bytes per lane, through LDS
+    // (a lane holds single values of 16 rows)
+    static_assert(NI * 32 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
+    __syncthreads();   // every wavefront is done with the ring
+    bf16_t* stg = lds + wave * (MI * 32 * DX_PITCH);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          stg[(mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * DX_PITCH + ni * 32 + lr] = f32_to_bf16(acc[mi][ni][r]);
+    // (the wavefront reads back only what it wrote; its LDS operations complete in order)
+    __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
+    __builtin_amdgcn_wave_barrier();
+    bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+    const int col = n0 + wn * NI * 32 + (lane & 7) * 8;   // N = H is a multiple of 64: whole segment or none
+#pragma unroll
+    for (int it = 0; it < MI * 32 / 8; ++it) {
+      const int lr2 = it * 8 + (lane >> 3);
+      const int i = wm * MI * 32 + lr2;
+      const uint4 v = *reinterpret_cast<const uint4*>(stg + lr2 * DX_PITCH + (lane & 7) * 8);
+      if (i < mvalid && col < N) *reinterpret_cast<uint4*>(out + (m0 + i) * (int64_t)N + col) = v;
+    }
+    return;
+  }
   // The weight gradients (45 GB of fp32 at the V3-like shape, never re-read by
   // this layer) are stored non-temporally: measured 2-5% faster than plain
   // stores, which also displace the operand panels from the L2.
@@ -387,8 +419,6 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
           dgu[at] = f32_to_bf16(v * u * (sg + g * sg * (1.0f - sg)));
           dgu[at + p.I] = f32_to_bf16(v * silu);
           (shared ? p.h_shared : p.h_routed)[row * N + col] = f32_to_bf16(silu * u);
-        } else if constexpr (KIND == kDx) {
-          static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed)[row * N + col] = f32_to_bf16(v);
         } else if constexpr (KIND == kDxR) {
           static_cast<float*>(p.out_shared)[row * N + col] = v;
         } else if constexpr (KIND == kDwGu) {
