@@ -299,42 +299,51 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] holds C[i][j] with j = lane % 32 and
   // i = 8 * (r / 4) + 4 * (lane / 32) + r % 4 inside the 32 x 32 block.
-  // kRouterTopk reuses the LDS ring for the [BM][BN] fp32 affinities: every
-  // wavefront must be done with its last slice first.
-  if constexpr (MODE == kGateUp) {
-    // h = silu(g) * u for the tile's BM rows x BN/2 columns, assembled in LDS over
-    // the finished ring (rows padded to kGateUpStagePitch elements) and stored as
-    // whole 256-byte row segments, 16 bytes per lane.
+  if constexpr (is_gate_up(MODE)) {
+    // The tile's outputs over BM rows x BN/2 columns -- h = silu(g) * u, and the
+    // gate and up outputs g, u themselves where the mode keeps them -- are
+    // assembled in LDS one after the other over the finished ring (rows padded to
+    // kGateUpStagePitch elements) and stored as whole 256-byte row segments, 16
+    // bytes per lane.
     constexpr int HALF = NI / 2;
     constexpr int HC = BN / 2;                      // h columns of the tile
-    static_assert(HC * 2 == 256 && BM * kGateUpStagePitch <= STAGES * STAGE, "h tile staging");
-    __syncthreads();   // every wavefront is done with the ring
+    static_assert(HC * 2 == 256 && BM * kGateUpStagePitch <= STAGES * STAGE, "output tile staging");
+    constexpr int NOUT = MODE == kGateUp ? 1 : MODE == kGateUpGU ? 2 : 3;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+    for (int o = 0; o < NOUT; ++o) {
+      // output o: kGateUp h; kGateUpGU g, u; kGateUpSave h, g, u
+      const int what = MODE == kGateUpGU ? o + 1 : o;   // 0 h, 1 g, 2 u
+      __syncthreads();   // the ring (o == 0), or the previous output's stores, are done with the stage
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < HALF; ++ni) {
-          const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
-          lds[i * kGateUpStagePitch + wn * HALF * 32 + ni * 32 + lr] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
+        for (int r = 0; r < 16; ++r) {
+          const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+#pragma unroll
+          for (int ni = 0; ni < HALF; ++ni) {
+            const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
+            const float v = what == 0 ? g / (1.0f + __expf(-g)) * u : what == 1 ? g : u;
+            lds[i * kGateUpStagePitch + wn * HALF * 32 + ni * 32 + lr] = f32_to_bf16(v);
+          }
         }
-      }
-    __syncthreads();
-    bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
-    if (nt * HC < ncols) {   // ncols (I or S*I) is a multiple of 128: the tile's columns are all valid or none
-      for (int q = threadIdx.x; q < BM * (HC / 8); q += NT) {
-        const int rr = q / (HC / 8), ch = q % (HC / 8);
-        if (rr < rows)
-          *reinterpret_cast<uint4*>(out + (row0 + rr) * (int64_t)ncols + nt * HC + ch * 8) =
-              *reinterpret_cast<const uint4*>(lds + rr * kGateUpStagePitch + ch * 8);
+      __syncthreads();
+      bf16_t* out = what == 0 ? static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed)
+                  : what == 1 ? (shared ? p.g_shared : p.g_routed)
+                              : (shared ? p.u_shared : p.u_routed);
+      if (nt * HC < ncols) {   // ncols (I or S*I) is a multiple of 128: the tile's columns are all valid or none
+        for (int q = threadIdx.x; q < BM * (HC / 8); q += NT) {
+          const int rr = q / (HC / 8), ch = q % (HC / 8);
+          if (rr < rows)
+            *reinterpret_cast<uint4*>(out + (row0 + rr) * (int64_t)ncols + nt * HC + ch * 8) =
+                *reinterpret_cast<const uint4*>(lds + rr * kGateUpStagePitch + ch * 8);
+        }
       }
     }
     return;
   }
   if constexpr (MODE == kDown) {
     // A lane holds single values of 16 rows; the wavefront's (MI*32) x (NI*32)
-    // outputs pass through LDS (rows padded to DSP elements against bank
+    // outputs pass through LDS (rows padded to kDownStagePitch elements against bank
     // conflicts, over the finished ring) and go out as whole 128-byte row
     // segments, 16 bytes per lane.
     static_assert(NI * 32 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
@@ -362,6 +371,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
     }
     return;
   }
+  // kRouterTopk reuses the LDS ring for the [BM][BN] fp32 affinities: every
+  // wavefront must be done with its last slice first.
   if constexpr (MODE == kRouterTopk) __syncthreads();
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -370,24 +381,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
       const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
       if (i >= rows) continue;
       const int64_t row = row0 + i;
-      if constexpr (is_gate_up(MODE)) {
-        constexpr int HALF = NI / 2;
-        bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
-        bf16_t* og = shared ? p.g_shared : p.g_routed;
-        bf16_t* ou = shared ? p.u_shared : p.u_routed;
-#pragma unroll
-        for (int ni = 0; ni < HALF; ++ni) {
-          const int col = nt * (BN / 2) + wn * HALF * 32 + ni * 32 + lr;
-          const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
-          if (col < ncols) {
-            if constexpr (MODE != kGateUpGU) out[row * ncols + col] = f32_to_bf16(g / (1.0f + __expf(-g)) * u);
-            if constexpr (MODE != kGateUp) {
-              og[row * ncols + col] = f32_to_bf16(g);
-              ou[row * ncols + col] = f32_to_bf16(u);
-            }
-          }
-        }
-      } else if constexpr (MODE == kRouterTopk) {
+      if constexpr (MODE == kRouterTopk) {
         // the tile holds every expert of its tokens (nt == 0, BN >= E)
         float* sl = reinterpret_cast<float*>(lds);
         float* out = static_cast<float*>(p.out_routed);
