@@ -85,10 +85,14 @@ static_assert(kDecBNH == kBNH, "h column tiles of both bf16 configurations (I % 
 inline bool small_batch(const moe_cfg* c) {
   return c->act == MOE_BF16 && c->wgt == MOE_BF16 && pairs(c) <= (int64_t)kDecBM * c->E;
 }
-// FP8 GEMMs: 256 token rows; 128 h columns (one 1 x 128 quantisation tile of
-// h) per gate/up tile, 256 output columns per down tile, K at most kFp8MaxKC
-// chunks of 128.
-constexpr int kFp8BM = 256;
+// FP8 GEMMs: 320 token rows (10 row blocks of 16 per wavefront, the most that
+// 256 registers hold; 4% faster down and 1% faster gate/up than 256 rows at the
+// FP8 workload); 128 h columns (one 1 x 128 quantisation tile of h) per gate/up
+// tile, 256 output columns per down tile, K at most kFp8MaxKC chunks of 128.
+#ifndef MOE_FP8_BM
+#define MOE_FP8_BM 320
+#endif
+constexpr int kFp8BM = MOE_FP8_BM;
 constexpr int kFp8BNH = 128;
 constexpr int kFp8BN2 = 256;
 constexpr int kFp8MaxKC = 64;

@@ -44,8 +44,8 @@ namespace {
 
 enum { kGateUp8 = 1, kDown8 = 2 };
 
-// FP8 tile: 2 x 4 wavefronts of 8 x 4 blocks (128 x 64 each) -> 256 x 256
-constexpr int kWM8 = 2, kWN8 = 4, kMI8 = 8, kNI8 = 4;
+// FP8 tile: 2 x 4 wavefronts of 10 x 4 blocks (160 x 64 each) -> 320 x 256
+constexpr int kWM8 = 2, kWN8 = 4, kMI8 = kFp8BM / (kWM8 * 16), kNI8 = 4;
 static_assert(kWM8 * kMI8 * 16 == kFp8BM, "row tiles of the fp8 tile table");
 static_assert(kWN8 * kNI8 * 16 == 2 * kFp8BNH && kWN8 * kNI8 * 16 == kFp8BN2, "column tiles");
 
@@ -130,7 +130,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   // down epilogue: each wavefront stages its (MI*16) x (NI*16) bf16 outputs in LDS
   // (rows padded to STG_PITCH bytes against bank conflicts) over the finished ring
   constexpr int STG_PITCH = NI * 16 * 2 + 16;
-  constexpr int STG_BYTES = MODE == kDown8 ? NW * MI * 16 * STG_PITCH : 0;
+  // row blocks staged per round (the whole wavefront tile when it fits in 144 KB)
+  constexpr int STG_MI = NW * MI * 16 * STG_PITCH <= 147456 ? MI : MI / 2;
+  static_assert(MI % STG_MI == 0, "whole staging rounds");
+  constexpr int STG_BYTES = MODE == kDown8 ? NW * STG_MI * 16 * STG_PITCH : 0;
   constexpr int LDS_BYTES = RED_OFF + BM * WN * 4 > STG_BYTES ? RED_OFF + BM * WN * 4 : STG_BYTES;
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
@@ -411,24 +414,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     // of its time in the epilogue.)
     static_assert(NI * 16 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
     __syncthreads();   // every wavefront is done with the ring
-    uint8_t* stg = lds + wave * (MI * 16 * STG_PITCH);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        *reinterpret_cast<uint2*>(stg + (mi * 16 + l16) * STG_PITCH + (ni * 16 + 4 * g) * 2) =
-            uint2{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
-    // (the wavefront reads back only what it wrote; its LDS operations complete in order)
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
+    uint8_t* stg = lds + wave * (STG_MI * 16 * STG_PITCH);
     bf16_t* out = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
     const int col = nt * BN + wn * NI * 16 + (lane & 7) * 8;   // ncols is a multiple of 128: the segment is whole or absent
 #pragma unroll
-    for (int it = 0; it < MI * 16 / 8; ++it) {
-      const int lr = it * 8 + (lane >> 3);
-      const int i = wm * MI * 16 + lr;
-      const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * STG_PITCH + (lane & 7) * 16);
-      if (i < rows && col < ncols) *reinterpret_cast<uint4*>(out + (row0 + i) * (int64_t)ncols + col) = v;
+    for (int m0 = 0; m0 < MI; m0 += STG_MI) {
+#pragma unroll
+      for (int mi = m0; mi < m0 + STG_MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          *reinterpret_cast<uint2*>(stg + ((mi - m0) * 16 + l16) * STG_PITCH + (ni * 16 + 4 * g) * 2) =
+              uint2{pack_bf16x2(acc[mi][ni][0], acc[mi][ni][1]), pack_bf16x2(acc[mi][ni][2], acc[mi][ni][3])};
+      // (the wavefront reads back only what it wrote; its LDS operations complete in order)
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < STG_MI * 16 / 8; ++it) {
+        const int lr = it * 8 + (lane >> 3);
+        const int i = wm * MI * 16 + m0 * 16 + lr;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + lr * STG_PITCH + (lane & 7) * 16);
+        if (i < rows && col < ncols) *reinterpret_cast<uint4*>(out + (row0 + i) * (int64_t)ncols + col) = v;
+      }
+      // (the next round's stage writes come after these reads in this wavefront's LDS order)
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
     }
   }
 #endif
