@@ -99,11 +99,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
   static_assert(BM * CPK % NT == 0 && BN * CPK % NT == 0, "whole loads per thread");
   static_assert(BM % 128 == 0 && BN % 128 == 0, "M-contiguous slices of at least 16 chunks per row");
 #if defined(__HIP_DEVICE_COMPILE__)
-  // kDx: each wavefront's (MI*32) x (NI*32) outputs are staged in LDS for the
-  // epilogue (rows padded to DX_PITCH elements), over the finished ring
+  // kDx, kDh: each wavefront's (MI*32) x (NI*32) outputs are staged in LDS for
+  // the epilogue (rows padded to DX_PITCH elements), over the finished ring
   constexpr int DX_PITCH = NI * 32 + 8;
-  constexpr int LDS_ELEMS = KIND == kDx && NW * MI * 32 * DX_PITCH > STAGES * STAGE ? NW * MI * 32 * DX_PITCH
-                                                                                     : STAGES * STAGE;
+  constexpr bool STAGED = KIND == kDx || KIND == kDh;
+  constexpr int LDS_ELEMS = STAGED && NW * MI * 32 * DX_PITCH > STAGES * STAGE ? NW * MI * 32 * DX_PITCH
+                                                                              : STAGES * STAGE;
   __shared__ __attribute__((aligned(16))) bf16_t lds[LDS_ELEMS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -366,6 +367,83 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
 
   // ------------------------------------------------------------ epilogue
   // acc[mi][ni][r] = C[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  if constexpr (KIND == kDh) {
+    // SwiGLU backward from the recomputed g, u: dg = dh u silu'(g), du = dh silu(g),
+    // and h = silu(g) u.  The three outputs go out one after the other as whole
+    // 128-byte row segments through LDS; du and h wait, rounded to bf16, in the
+    // accumulator registers.
+    static_assert(NI * 32 * 2 == 128, "a wavefront's columns are one 128-byte row segment");
+    const bf16_t* G = shared ? p.g_shared : p.g_routed;
+    const bf16_t* U = shared ? p.u_shared : p.u_routed;
+    const int c0 = n0 + wn * NI * 32;   // first column of this wavefront (in one I block: I % 128 == 0)
+    __syncthreads();   // every wavefront is done with the ring
+    bf16_t* stg = lds + wave * (MI * 32 * DX_PITCH);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      // this row block's g and u: all loads issued before any is used
+      float gv[16][NI], uv[16][NI];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = wm * MI * 32 + mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const int64_t row = m0 + (i < mvalid ? i : 0);    // rows past the tile's end read row 0 (never stored)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const int col = min(c0 + ni * 32 + lr, N - 1);
+          gv[r][ni] = bf16_to_f32(G[row * N + col]);
+          uv[r][ni] = bf16_to_f32(U[row * N + col]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const float v = acc[mi][ni][r], g = gv[r][ni], u = uv[r][ni];
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float silu = g * sg;
+          stg[(mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * DX_PITCH + ni * 32 + lr] =
+              f32_to_bf16(v * u * (sg + g * sg * (1.0f - sg)));
+          uint32_t duh = pack_bf16x2(v * silu, silu * u);   // (du, h), kept here: an opaque
+          asm volatile("" : "+v"(duh));                      // copy so that it is not recomputed later
+          acc[mi][ni][r] = __uint_as_float(duh);
+        }
+    }
+    bf16_t* dgu = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
+    bf16_t* hh = shared ? p.h_shared : p.h_routed;
+    const int64_t dcol = (c0 / p.I) * 2 * p.I + c0 % p.I;   // dg of column c0 in a row of [g | u] blocks
+#pragma unroll
+    for (int o = 0; o < 3; ++o) {   // 0 dg, 1 du, 2 h
+      if (o > 0) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t w = __float_as_uint(acc[mi][ni][r]);
+              stg[(mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * DX_PITCH + ni * 32 + lr] =
+                  (bf16_t)(o == 1 ? (w & 0xFFFFu) : (w >> 16));
+            }
+      }
+      // (the wavefront reads back only what it wrote; its LDS operations complete in order)
+      __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < MI * 32 / 8; ++it) {
+        const int lr2 = it * 8 + (lane >> 3);
+        const int i = wm * MI * 32 + lr2;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + lr2 * DX_PITCH + (lane & 7) * 8);
+        if (i < mvalid && c0 < N) {
+          const int64_t row = m0 + i;
+          bf16_t* dst = o == 2 ? hh + row * N + c0 : dgu + row * 2 * N + dcol + (o == 1 ? p.I : 0);
+          *reinterpret_cast<uint4*>(dst + (lane & 7) * 8) = v;
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kLgkmWaitZero);
+      __builtin_amdgcn_wave_barrier();
+    }
+    return;
+  }
   if constexpr (KIND == kDx) {
     // dX goes out as whole 128-byte row segments, 16 bytes per lane, through LDS
     // (a lane holds single values of 16 rows)
@@ -408,18 +486,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
         const int col = n0 + wn * NI * 32 + ni * 32 + lr;
         if (col >= N) continue;
         const float v = acc[mi][ni][r];
-        if constexpr (KIND == kDh) {
-          const bf16_t* G = shared ? p.g_shared : p.g_routed;
-          const bf16_t* U = shared ? p.u_shared : p.u_routed;
-          const float g = bf16_to_f32(G[row * N + col]), u = bf16_to_f32(U[row * N + col]);
-          const float sg = 1.0f / (1.0f + __expf(-g));
-          const float silu = g * sg;
-          bf16_t* dgu = static_cast<bf16_t*>(shared ? p.out_shared : p.out_routed);
-          const int64_t at = row * 2 * N + (col / p.I) * 2 * p.I + col % p.I;
-          dgu[at] = f32_to_bf16(v * u * (sg + g * sg * (1.0f - sg)));
-          dgu[at + p.I] = f32_to_bf16(v * silu);
-          (shared ? p.h_shared : p.h_routed)[row * N + col] = f32_to_bf16(silu * u);
-        } else if constexpr (KIND == kDxR) {
+        if constexpr (KIND == kDxR) {
           static_cast<float*>(p.out_shared)[row * N + col] = v;
         } else if constexpr (KIND == kDwGu) {
           float* o = shared ? static_cast<float*>(p.out_shared)
