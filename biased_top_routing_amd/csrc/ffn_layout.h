@@ -109,33 +109,57 @@ struct TileDesc {
   int32_t seg, row0, rows, nt;
 };
 
+// How a grouped launch deals its routed tiles to the XCDs (workgroup id mod 8):
+// 0 gives each XCD one contiguous share of the table, so an expert's tiles all
+// run in one XCD's L2; P > 0 deals runs of P consecutive table entries to the
+// 8 XCDs in turn, so the XCDs work on neighbouring table entries at the same
+// time: an expert's column tiles then run on several XCDs together, reading its
+// activation rows once from memory and the rest from the memory-side cache,
+// and each run of P still shares weight panels in one L2.  Measured at the
+// V3-like shapes (alternating libraries on one box): gate/up bf16 runs of 8
+// 1-1.5% faster than contiguous shares (2: 1% slower, 32 or more: slower);
+// FP8 runs of 2 5% (gate/up) and 7% (down) faster (1: equal, 8: 2-3%); the
+// bf16 down GEMM is fastest with contiguous shares (runs of 2-64: 1-4% slower).
+constexpr int kStripeGateUp = 8;
+constexpr int kStripeDown = 0;
+constexpr int kStripeFp8 = 2;
+
 #if defined(__HIP_DEVICE_COMPILE__)
 // Grouped GEMM launches: one workgroup per tile of a device-built table that
 // holds ntiles[4] routed tiles followed by the shared-expert ones (ntiles[0] in
-// all).  Each XCD (workgroup id mod 8) takes an equal contiguous share of the
-// shared tiles first, then one of the routed tiles: tiles sharing operands run
-// together in one XCD's L2, and the shared tiles, all full, are spread over
-// every XCD (cut by count alone, the table left the shared tiles to the last
-// XCD, which then finished last).  Returns the table position of this
-// workgroup's tile, or -1 for a surplus workgroup.
+// all).  Each XCD takes an equal contiguous share of the shared tiles first
+// (all full; cut by count alone, the table left them to the last XCD, which
+// then finished last), then its routed tiles as P says (above).  Returns the
+// table position of this workgroup's tile, or -1 for a surplus workgroup.
+template <int P>
 __device__ __forceinline__ int grouped_tile(const int32_t* ntiles) {
+  static_assert(P >= 0, "run length");
   const int n_real = __builtin_amdgcn_readfirstlane(ntiles[0]);
   const int n_rt = __builtin_amdgcn_readfirstlane(ntiles[4]);
-  const int per_s = (n_real - n_rt + 7) >> 3, per_r = (n_rt + 7) >> 3;
+  const int per_s = (n_real - n_rt + 7) >> 3;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   if (j < per_s) {
     const int L = n_rt + xcd * per_s + j;
     return L < n_real ? L : -1;
   }
-  const int L = xcd * per_r + (j - per_s);
-  return j - per_s < per_r && L < n_rt ? L : -1;
+  const int jr = j - per_s;
+  if constexpr (P > 0) {
+    const int L = (jr / P) * (8 * P) + xcd * P + jr % P;
+    return L < n_rt ? L : -1;
+  } else {
+    const int per_r = (n_rt + 7) >> 3;
+    const int L = xcd * per_r + jr;
+    return jr < per_r && L < n_rt ? L : -1;
+  }
 }
 #endif
 
-// Workgroups of a grouped launch over a table of at most max_tiles tiles (the
-// two shares of an XCD round up apart: two more per XCD).
-inline int64_t grouped_grid(int64_t max_tiles) {
-  return max_tiles > 0 ? (int64_t)align_up((size_t)max_tiles, 8) + 16 : 0;
+// Workgroups of a grouped launch over a table of at most max_tiles tiles, with
+// the kernel's run length P: an XCD takes ceil(shared / 8) shared positions and
+// ceil(routed / 8) (P = 0) or P * ceil(routed / 8P) (at most routed / 8 + P)
+// routed ones, so P + 2 positions per XCD beyond max_tiles / 8 cover both.
+inline int64_t grouped_grid(int64_t max_tiles, int P) {
+  return max_tiles > 0 ? (int64_t)align_up((size_t)max_tiles, 8) + 8 * (P + 2) : 0;
 }
 
 struct FfnLayout {

@@ -431,7 +431,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bf16_kernel(GemmParams
     rows = min(BM, p.T - row0);
     nt = blockIdx.y;
   } else {
-    const int L = grouped_tile(p.ntiles);
+    const int L = grouped_tile<is_gate_up(MODE) ? kStripeGateUp : kStripeDown>(p.ntiles);
     if (L < 0) return;
     const TileDesc d = p.tiles[L];
     // the descriptor is the same for the whole workgroup: keep it in SGPRs
@@ -697,7 +697,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
       p.g_shared = static_cast<bf16_t*>(saved->gs); p.u_shared = static_cast<bf16_t*>(saved->us);
     }
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
-    const int64_t grid = grouped_grid(L.max1);
+    const int64_t grid = grouped_grid(L.max1, kStripeGateUp);
     if (grid > 0) {
       const dim3 dg((unsigned)grid), bd(64 * DecGateUpTile::WM * DecGateUpTile::WN),
           bg(64 * GateUpTile::WM * GateUpTile::WN);
@@ -717,7 +717,7 @@ moe_status launch_ffn_bf16(const moe_cfg* c, const bf16_t* x_perm, const int32_t
     p.tiles = reinterpret_cast<const TileDesc*>(base + L.off_t2);
     p.ntiles = hdr + 1;
     p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I;
-    const int64_t grid = grouped_grid(L.max2);
+    const int64_t grid = grouped_grid(L.max2, kStripeDown);
     if (grid > 0) {
       if (L.dec)
         hipLaunchKernelGGL((gemm_bf16_kernel<kDown, MOE_DEC_DN_TILE>), dim3((unsigned)grid),
@@ -743,7 +743,7 @@ moe_status launch_gateup_recompute_bf16(const moe_cfg* c, const bf16_t* x_perm, 
   p.tiles = tiles;
   p.ntiles = ntiles;
   p.T = c->T; p.H = c->H; p.E = c->E; p.S = c->S; p.I = c->I; p.k = c->k;
-  const int64_t grid = grouped_grid(max_tiles);
+  const int64_t grid = grouped_grid(max_tiles, kStripeGateUp);
   if (grid > 0)
     hipLaunchKernelGGL((gemm_bf16_kernel<kGateUpGU, MOE_GU_TILE, MOE_GU_MI_ALT>), dim3((unsigned)grid),
                        dim3(64 * GateUpTile::WM * GateUpTile::WN), 0, st, p);

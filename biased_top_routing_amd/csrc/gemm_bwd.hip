@@ -131,7 +131,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
     ldb = p.H;
     b_bytes = p.E * p.H * 2;
   } else if constexpr (!KSEG) {
-    const int L = grouped_tile(p.ntiles);
+    const int L = grouped_tile<0>(p.ntiles);
     if (L < 0) return;
     const TileDesc d = p.tiles[L];
     seg = __builtin_amdgcn_readfirstlane(d.seg);
@@ -572,7 +572,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   p.g_routed = g; p.g_shared = gs; p.u_routed = u; p.u_shared = us;
   p.out_routed = dgu; p.out_shared = dgus; p.h_routed = h; p.h_shared = hs;
   p.tiles = t_dh; p.ntiles = hdr + 2;
-  hipLaunchKernelGGL((gemm_bwd_kernel<kDh, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dh)), dim3(kBwdThreads), 0,
+  hipLaunchKernelGGL((gemm_bwd_kernel<kDh, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dh, 0)), dim3(kBwdThreads), 0,
                      st, p);
   if ((s = launch_status()) != MOE_OK) return s;
   // dx
@@ -580,7 +580,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   p.b_routed = (const bf16_t*)w->w_gate_up; p.b_shared = (const bf16_t*)w->ws_gate_up;
   p.out_routed = dx_perm; p.out_shared = dx_shared;
   p.tiles = t_dx; p.ntiles = hdr + 1;
-  hipLaunchKernelGGL((gemm_bwd_kernel<kDx, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dx)), dim3(kBwdThreads), 0,
+  hipLaunchKernelGGL((gemm_bwd_kernel<kDx, MOE_BWD_TILE>), dim3((unsigned)grouped_grid(L.max_dx, 0)), dim3(kBwdThreads), 0,
                      st, p);
   if ((s = launch_status()) != MOE_OK) return s;
   // weight gradients
