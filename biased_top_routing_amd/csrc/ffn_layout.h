@@ -118,7 +118,7 @@ struct TileDesc {
 // and each run of P still shares weight panels in one L2.  Measured at the
 // V3-like shapes (alternating libraries on one box): gate/up bf16 runs of 8
 // 1-1.5% faster than contiguous shares (2: 1% slower, 32 or more: slower);
-// FP8 runs of 2 5% (gate/up) and 7% (down) faster (1: equal, 8: 2-3%); the
+// FP8 runs of 2 2-5% (gate/up) and 6-8% (down) faster (1 or 8: 0-3%); the
 // bf16 down GEMM is fastest with contiguous shares (runs of 2-64: 1-4% slower).
 constexpr int kStripeGateUp = 8;
 constexpr int kStripeDown = 0;
