@@ -124,33 +124,42 @@ constexpr int kStripeGateUp = 8;
 constexpr int kStripeDown = 0;
 constexpr int kStripeFp8 = 2;
 
-#if defined(__HIP_DEVICE_COMPILE__)
+// Position j of XCD xcd in runs of P consecutive entries dealt to the 8 XCDs in turn.
+__host__ __device__ inline int xcd_run_index(int j, int xcd, int P) {
+  return (j / P) * (8 * P) + xcd * P + j % P;
+}
+
 // Grouped GEMM launches: one workgroup per tile of a device-built table that
-// holds ntiles[4] routed tiles followed by the shared-expert ones (ntiles[0] in
-// all).  Each XCD takes an equal contiguous share of the shared tiles first
-// (all full; cut by count alone, the table left them to the last XCD, which
-// then finished last), then its routed tiles as P says (above).  Returns the
-// table position of this workgroup's tile, or -1 for a surplus workgroup.
-template <int P>
-__device__ __forceinline__ int grouped_tile(const int32_t* ntiles) {
-  static_assert(P >= 0, "run length");
-  const int n_real = __builtin_amdgcn_readfirstlane(ntiles[0]);
-  const int n_rt = __builtin_amdgcn_readfirstlane(ntiles[4]);
+// holds n_rt routed tiles followed by the shared-expert ones (n_real in all).
+// Each XCD (workgroup id b mod 8) takes an equal contiguous share of the
+// shared tiles first (all full; cut by count alone, the table left them to the
+// last XCD, which then finished last), then its routed tiles as P says
+// (above).  Returns the table position of workgroup b's tile, or -1 for a
+// surplus workgroup.
+__host__ __device__ inline int grouped_tile_at(int b, int n_real, int n_rt, int P) {
   const int per_s = (n_real - n_rt + 7) >> 3;
-  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int xcd = b & 7, j = b >> 3;
   if (j < per_s) {
     const int L = n_rt + xcd * per_s + j;
     return L < n_real ? L : -1;
   }
   const int jr = j - per_s;
-  if constexpr (P > 0) {
-    const int L = (jr / P) * (8 * P) + xcd * P + jr % P;
+  if (P > 0) {
+    const int L = xcd_run_index(jr, xcd, P);
     return L < n_rt ? L : -1;
-  } else {
-    const int per_r = (n_rt + 7) >> 3;
-    const int L = xcd * per_r + jr;
-    return jr < per_r && L < n_rt ? L : -1;
   }
+  const int per_r = (n_rt + 7) >> 3;
+  const int L = xcd * per_r + jr;
+  return jr < per_r && L < n_rt ? L : -1;
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// This workgroup's table position (ntiles[0] tiles in all, ntiles[4] routed).
+template <int P>
+__device__ __forceinline__ int grouped_tile(const int32_t* ntiles) {
+  static_assert(P >= 0, "run length");
+  return grouped_tile_at(blockIdx.x, __builtin_amdgcn_readfirstlane(ntiles[0]),
+                         __builtin_amdgcn_readfirstlane(ntiles[4]), P);
 }
 #endif
 

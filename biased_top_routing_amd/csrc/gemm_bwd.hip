@@ -39,8 +39,7 @@
 namespace moe {
 
 enum { kDh = 0, kDx = 1, kDxR = 2, kDwGu = 3, kDwD = 4, kDwR = 5 };
-// Routed weight-gradient tiles dealt to the XCDs in runs of this many (see the tile mapping below).
-constexpr int dw_stripe(int kind) { return kind == kDwGu ? 32 : 8; }
+constexpr int dw_stripe(int kind) { return kind == kDwGu ? kStripeDwGu : kStripeDwD; }
 constexpr bool kseg_kind(int kind) { return kind >= kDwGu; }
 
 struct BwdParams {
@@ -182,30 +181,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
       const int Ms = KIND == kDwGu ? p.S * 2 * p.I : p.H, Ns = KIND == kDwGu ? p.H : p.S * p.I;
       const int mtr = (Mr + BM - 1) / BM, ntr = (Nr + BN - 1) / BN;
       const int n_sh = p.S > 0 ? ((Ms + BM - 1) / BM) * ((Ns + BN - 1) / BN) : 0;
-      const int n_sh8 = (n_sh + 7) & ~7;          // padded to whole XCD rounds
-      // the shared experts' tiles (K = T, the longest) come first, one per
-      // workgroup id, so that they spread over all XCDs and start early; the
-      // routed tiles follow in runs of PW consecutive tiles dealt to the 8
-      // XCDs in turn, so that the XCDs work on one expert's tiles together and
-      // its operand rows, missed by every XCD's L2 within a short time, come
-      // from the memory-side cache (against one contiguous range per XCD:
-      // dW_gate_up 2-3% faster with runs of 32, dW_down 3% with runs of 8)
-      if ((int)blockIdx.x < n_sh8) {
-        if ((int)blockIdx.x >= n_sh) return;
+      const int nrt = p.E * mtr * ntr;
+      const int q = dw_tile_at(blockIdx.x, n_sh, nrt, dw_stripe(KIND));
+      if (q < 0) return;
+      if (q < n_sh) {
         shared = true;
         seg = p.E;
         M = Ms;
         N = Ns;
         ntn = (Ns + BN - 1) / BN;
-        local = blockIdx.x;
+        local = q;
         K = p.T;
       } else {
-        const int b = blockIdx.x - n_sh8;       // a multiple of 8 earlier: b % 8 is still the XCD
-        const int nrt = p.E * mtr * ntr;
-        constexpr int PW = dw_stripe(KIND);
-        const int xcd = b & 7, j = b >> 3;
-        const int L = (j / PW) * (8 * PW) + xcd * PW + j % PW;
-        if (L >= nrt) return;
+        const int L = q - n_sh;
         seg = L / (mtr * ntr);
         local = L % (mtr * ntr);
         M = Mr;
@@ -597,7 +585,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   p.out_routed = gr->w_gate_up; p.out_shared = gr->ws_gate_up;
   {
     const int64_t n_sh = c->S > 0 ? tiles_of(2 * SI, c->H) : 0;
-    const int64_t n = grid_of(n_sh) + grid_of(c->E * tiles_of(2 * c->I, c->H)) + 8 * dw_stripe(kDwGu);
+    const int64_t n = dw_grid(n_sh, c->E * tiles_of(2 * c->I, c->H), dw_stripe(kDwGu));
     hipLaunchKernelGGL((gemm_bwd_kernel<kDwGu, MOE_BWD_WG_TILE>), dim3((unsigned)n), dim3(WgTile::THREADS), 0, st, p);
     if ((s = launch_status()) != MOE_OK) return s;
   }
@@ -606,7 +594,7 @@ moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf1
   p.out_routed = gr->w_down; p.out_shared = gr->ws_down;
   {
     const int64_t n_sh = c->S > 0 ? tiles_of(c->H, SI) : 0;
-    const int64_t n = grid_of(n_sh) + grid_of(c->E * tiles_of(c->H, c->I)) + 8 * dw_stripe(kDwD);
+    const int64_t n = dw_grid(n_sh, c->E * tiles_of(c->H, c->I), dw_stripe(kDwD));
     hipLaunchKernelGGL((gemm_bwd_kernel<kDwD, MOE_BWD_WG_TILE>), dim3((unsigned)n), dim3(WgTile::THREADS), 0, st, p);
     if ((s = launch_status()) != MOE_OK) return s;
   }
