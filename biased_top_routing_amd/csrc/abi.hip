@@ -1,5 +1,7 @@
 // Host side of the C ABI: configuration checks, workspace sizing, status text.
 // Everything here runs before any device call, so it also works without a GPU.
+#include <algorithm>
+
 #include "common.h"
 #include "bwd_layout.h"
 #include "ffn_layout.h"
@@ -31,6 +33,11 @@ moe_status validate_cfg(const moe_cfg* c) {
   // one buffer descriptor covers a segment's weights (all shared experts together)
   if ((int64_t)(c->S > 1 ? c->S : 1) * 2 * c->I * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if ((int64_t)c->E * c->H * 2 >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  // the grouped GEMMs' tile tables and launch grids count tiles in 32 bits (tiles
+  // of at least 32 rows x 64 columns, plus a ragged one per segment)
+  const int64_t rows = (int64_t)c->T * (c->k + c->S);
+  const int64_t widest = std::max((int64_t)c->H, (int64_t)(c->S > 1 ? c->S : 1) * c->I);
+  if ((rows / 32 + c->E + 2) * (widest / 64 + 2) >= ((int64_t)1 << 30)) return MOE_ERR_SHAPE;
   if (c->act == MOE_F32) {
     if (c->H % 4 || c->I % 4) return MOE_ERR_SHAPE;
   } else if (c->wgt == MOE_BF16) {

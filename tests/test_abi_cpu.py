@@ -44,6 +44,9 @@ def _cfg(**kw):
     (dict(act="f32"), L.MOE_ERR_UNSUPPORTED),  # f32 act with bf16 weights
     (dict(bias_eq_mode=2), L.MOE_ERR_UNSUPPORTED),
     (dict(T=-1), L.MOE_ERR_SHAPE),
+    # 2^30 (token, slot) rows, H = 512, I = 65536: within the byte limits, but the
+    # grouped GEMMs' tile tables would count past 32 bits
+    (dict(T=1 << 27, k=8, S=0, H=512, I=1 << 16), L.MOE_ERR_SHAPE),
 ])
 def test_bad_config_rejected_everywhere(kw, status):
     cfg = _cfg(**kw)
