@@ -62,10 +62,16 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
  *              expert GEMMs only.
  *  bias_eq_mode: 0 - an expert whose load equals T*k/E counts as underloaded
  *              (+gamma), so every bias moves each step; 1 - it is left unchanged.
- * Supported ranges: 1 <= G <= 64, E % G == 0, E <= 512, 1 <= M <= G,
- *  1 <= k <= min(32, M*E/G), T >= 0, T*k < 2^31, H % 8 == 0 and I % 8 == 0
- *  (F32: H % 4 == 0, I % 4 == 0); BF16 expert GEMMs need H % 64 == 0 and
- *  I % 128 == 0; FP8 needs H % 128 == 0 and I % 128 == 0.
+ * Supported ranges (every call checks them first and returns MOE_ERR_SHAPE
+ *  outside them; MOE_ERR_UNSUPPORTED for another act/wgt pair or bias_eq_mode):
+ *  1 <= G <= 64, E % G == 0, E <= 512, 1 <= M <= G, 1 <= k <= min(32, M*E/G),
+ *  1 <= group_topr <= min(8, E/G), route_scale not NaN, T >= 0, S >= 0,
+ *  T*k < 2^31, T*k*H < 2^40, H, I and S*I at most 2^20, one routed expert's
+ *  gate/up weights (all shared experts' together) under 2^31 bytes in bf16,
+ *  E*H*2 < 2^31, and (T*(k+S)/32 + E + 2) * (max(H, S*I)/64 + 2) < 2^30 (the
+ *  grouped GEMMs count their tiles in 32 bits).  F32: H % 4 == 0, I % 4 == 0;
+ *  BF16 experts: H % 64 == 0, I % 128 == 0; FP8 experts: H % 128 == 0,
+ *  I % 128 == 0, H <= 8192 and max(S, 1)*I <= 8192 (64 scale blocks of K).
  */
 typedef struct {
   int32_t T, H, E, G, M, k, S, I;
