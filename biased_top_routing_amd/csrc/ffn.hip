@@ -20,10 +20,10 @@ namespace moe {
 // the row height bm of the GEMM the table is for.
 // Inside a segment the row tiles are cut into groups of kGroupRowTiles; a
 // group's tiles are listed column-tile-major.  Tiles that run at the same time
-// on one XCD (consecutive entries) then cover a few row tiles times a few
-// column tiles, so both their activation rows and their weight rows are
-// shared in that XCD's L2, also for segments far larger than the number of
-// tiles in flight.  Every workgroup computes the prefix sums over segments in LDS
+// on one XCD (consecutive entries, or runs of them: grouped_tile_at) then cover
+// a few row tiles times a few column tiles, so both their activation rows and
+// their weight rows are shared in that XCD's L2, also for segments far larger
+// than the number of tiles in flight.  Every workgroup computes the prefix sums over segments in LDS
 // (at most 513 segments) and writes its own share of the entries.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __restrict__ offsets, int E,
                                                            int S, int T, int bm1, int bm1_alt, int bm2,

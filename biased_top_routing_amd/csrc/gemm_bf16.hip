@@ -17,10 +17,13 @@
 // the BN/2 up rows of the same intermediate columns, each wavefront holding
 // matching gate and up blocks, so SwiGLU is applied in registers.
 // Grouped tiles come from a device-built table (segment, first row, rows,
-// column tile); each XCD (workgroup id mod 8) takes a contiguous share of its
-// shared-expert tiles and one of its routed tiles, so tiles sharing operands
-// run together in one XCD's L2.  A gate/up tile whose rows fit fewer padded
-// MFMA rows with MI_ALT row blocks per wavefront runs that body instead.
+// column tile); each XCD (workgroup id mod 8) takes a contiguous share of the
+// shared-expert tiles, then its routed tiles: runs of 8 consecutive entries
+// dealt to the XCDs in turn for gate/up, one contiguous share for down
+// (grouped_tile_at), so tiles sharing operands run together in one XCD's L2
+// and neighbouring XCDs read the same rows close in time.  A gate/up tile
+// whose rows fit fewer padded MFMA rows with MI_ALT row blocks per wavefront
+// runs that body instead.
 // Small batches route through a separate split-K router kernel (no LDS ring).
 #include "common.h"
 #include "ffn_layout.h"
