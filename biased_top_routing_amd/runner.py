@@ -186,3 +186,28 @@ class MoeLayerGPU:
         if gamma is not None:
             self.update_bias(bias, gamma)
         return self.y
+
+    # ---------------------------------------------------------------- HIP graph
+    def capture(self, x, bias, gamma=None):
+        """Record one forward() over the tensors x and bias (and the bias update when
+        gamma is set) into a HIP graph; replay() reruns it on whatever they then hold.
+        One graph serves every batch of this T: each launch is sized by capacity (the
+        grouped GEMMs' tile tables are built on the device from the batch's routing)
+        and no call allocates, copies or synchronises, so the recorded work is the
+        same kernels forward() launches.  A warm-up pass (no bias update) on a side
+        stream precedes the capture."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.forward(x, bias, None)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.forward(x, bias, gamma)
+        self.graph_inputs = (x, bias)
+        return self.graph
+
+    def replay(self):
+        """One replay of the captured step on the current stream; returns y."""
+        self.graph.replay()
+        return self.y
