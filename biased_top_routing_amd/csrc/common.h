@@ -13,6 +13,16 @@ typedef uint8_t fp8_t;     // raw OCP E4M3FN bytes
 
 constexpr int kWave = 64;
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Logistic sigmoid of a SwiGLU gate input: the hardware reciprocal (v_rcp_f32,
+// 1 ulp) of 1 + exp(-g) in place of an IEEE division, whose ~10 instructions
+// per element weighed on the GEMM epilogues (FP8 gate/up 2% faster).  g = -inf
+// or a large negative g gives 1 + exp(-g) = inf and a sigmoid of 0.
+__device__ __forceinline__ float gate_sigmoid(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+#endif
+
 // ----------------------------------------------------------------- host side
 moe_status validate_cfg(const moe_cfg* c);
 bool gemm_dtype_ok(const moe_cfg* c);

@@ -325,7 +325,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bf16_t* lds, int 
 #pragma unroll
           for (int ni = 0; ni < HALF; ++ni) {
             const float g = acc[mi][ni][r], u = acc[mi][ni + HALF][r];
-            const float v = what == 0 ? g / (1.0f + __expf(-g)) * u : what == 1 ? g : u;
+            const float v = what == 0 ? g * gate_sigmoid(g) * u : what == 1 ? g : u;
             lds[i * kGateUpStagePitch + wn * HALF * 32 + ni * 32 + lr] = f32_to_bf16(v);
           }
         }

@@ -391,7 +391,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_bwd_kernel(BwdParams p
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
           const float v = acc[mi][ni][r], g = gv[r][ni], u = uv[r][ni];
-          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float sg = gate_sigmoid(g);
           const float silu = g * sg;
           stg[(mi * 32 + 8 * (r >> 2) + 4 * kh + (r & 3)) * DX_PITCH + ni * 32 + lr] =
               f32_to_bf16(v * u * (sg + g * sg * (1.0f - sg)));

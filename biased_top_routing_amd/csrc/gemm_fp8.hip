@@ -373,7 +373,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[mi][b][r], uv = acc[mi][b + HALF][r];
-          const float h = gv / (1.0f + __expf(-gv)) * uv;
+          const float h = gv * gate_sigmoid(gv) * uv;
           acc[mi][b][r] = h;     // h replaces the gate accumulator
           m = fmaxf(m, fabsf(h));
         }
