@@ -523,7 +523,6 @@ struct BwdTile {
 };
 using WgTile = BwdTile<MOE_BWD_WG_TILE>;
 
-static inline unsigned grid_of(int64_t n) { return (unsigned)align_up((size_t)(n > 0 ? n : 0), 8); }
 
 moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf16_t* x, const int32_t* offsets,
                                const moe_expert_weights* w, const moe_ffn_saved* saved, const bf16_t* dy_perm,
