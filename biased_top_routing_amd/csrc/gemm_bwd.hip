@@ -523,7 +523,6 @@ struct BwdTile {
 };
 using WgTile = BwdTile<MOE_BWD_WG_TILE>;
 
-
 moe_status launch_ffn_bwd_bf16(const moe_cfg* c, const bf16_t* x_perm, const bf16_t* x, const int32_t* offsets,
                                const moe_expert_weights* w, const moe_ffn_saved* saved, const bf16_t* dy_perm,
                                const bf16_t* dy, bf16_t* dx_perm, bf16_t* dx_shared, const moe_expert_grads* gr,
