@@ -549,15 +549,15 @@ __global__ __launch_bounds__(64 * WM * WN) void router_topk_kernel(GemmParams p)
 #endif
 }
 
+// CUs of the device current at the first call (a thread-safe one-time query).
 static int cu_count() {
-  static int n_cu = 0;
-  if (n_cu == 0) {
+  static const int n_cu = [] {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || n <= 0)
       n = 256;
-    n_cu = n;
-  }
+    return n;
+  }();
   return n_cu;
 }
 
