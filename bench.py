@@ -488,7 +488,7 @@ def gemm_probe(c, w, kind, reps=8):
     return out
 
 
-def balance_trajectory(layer, c, w, steps):
+def balance_trajectory(layer, c, w, steps, note=None):
     """Per-step expert load over `steps` consecutive batches of the layer with the bias
     update between them.  Batch i's x is make_x(c, i) from the shared seeded generator
     (the oracle can replay every step); per step the max/mean, min/mean and the
@@ -512,14 +512,13 @@ def balance_trajectory(layer, c, w, steps):
             log(f"  balance step {step + 1}/{steps} ({time.perf_counter() - t0:.0f} s)")
     hot = int(np.argmax(counts))
     b_end = bias.cpu().numpy()
-    return {"steps": steps, "gamma": c.gamma, "x": "make_x(cfg, step): N(0,1) from the shared seeded generator",
-            "max_over_mean": mx, "min_over_mean": mn, "cv": cv,
-            "hottest_expert": hot, "hottest_expert_bias_start": float(w.bias0[hot]),
-            "hottest_expert_bias_end": float(b_end[hot]),
-            "note": ("with Zipf(1.5) logit offsets the hottest experts' offsets (up to +4.6) dwarf what "
-                     "100 steps of gamma = 1e-3 can move (0.1), so every token keeps choosing them and "
-                     "max/mean stays at T / (T k / E) = E / k = 32; the bias of each such expert falls by "
-                     "gamma every step")}
+    out = {"steps": steps, "gamma": c.gamma, "x": "make_x(cfg, step): N(0,1) from the shared seeded generator",
+           "max_over_mean": mx, "min_over_mean": mn, "cv": cv,
+           "hottest_expert": hot, "hottest_expert_bias_start": float(w.bias0[hot]),
+           "hottest_expert_bias_end": float(b_end[hot])}
+    if note:
+        out["note"] = note
+    return out
 
 
 def route_sweep(c, w, sizes=(16384, 65536, 262144), iters=10):
@@ -613,7 +612,8 @@ def permute_copy(c, w, x, iters=10):
 
 def small_workload(name, steps, warmup, balance_steps, gather=False):
     """One of the small configurations (tiny fp32, mid bf16): per-step time, rates, and
-    the max/mean load over `balance_steps` batches (fresh x from the shared generator)."""
+    the per-step load series over `balance_steps` batches with the bias update between
+    them (balance_trajectory)."""
     import torch
 
     from biased_top_routing_amd.runner import MoeLayerGPU
@@ -632,15 +632,7 @@ def small_workload(name, steps, warmup, balance_steps, gather=False):
            "layer_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
            "layer_frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / peak, 4),
            "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
-    bias = torch.from_numpy(w.bias0.copy()).cuda()
-    ratios = []
-    mean = c.T * c.k / c.E
-    for step in range(balance_steps):
-        layer.forward(to_dev(make_x(c, step)), bias, gamma=c.gamma)
-        ratios.append(float(layer.counts.max().item()) / mean)
-    out["balance"] = {"steps": balance_steps,
-                      "max_over_mean_at_step": {str(i): round(ratios[i - 1], 3)
-                                                for i in (1, 5, 10, 25, 50) if i <= balance_steps}}
+    out["balance"] = balance_trajectory(layer, c, w, balance_steps)
     return out
 
 
@@ -787,7 +779,12 @@ def main():
                             "max_over_mean_load": round(float(cnt.max() / (cf.T * cf.k / cf.E)), 3),
                             "stages_ms": {k: round(v, 4) for k, v in stf.items()}}
         log("extra: FP8 layer, 100 batches with the bias update between them")
-        extras["v3_fp8"]["balance"] = balance_trajectory(lf, cf, wf, cf.steps)
+        extras["v3_fp8"]["balance"] = balance_trajectory(
+            lf, cf, wf, cf.steps,
+            note=("with Zipf(1.5) logit offsets the hottest experts' offsets (up to +4.6) dwarf what "
+                  "100 steps of gamma = 1e-3 can move (0.1), so every token keeps choosing them and "
+                  "max/mean stays at T / (T k / E) = E / k = 32; the bias of each such expert falls by "
+                  "gamma every step"))
         del lf, xf
         torch.cuda.empty_cache()
         for name in ("tiny_fp32", "mid_bf16"):
