@@ -107,7 +107,13 @@ __device__ __forceinline__ i32x8_t frag(const uint8_t* rowp, int lo, int hi) {
   return i32x8_t{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 }
 
-template <int MODE, int WM, int WN, int MI, int NI, int STAGES>
+// SB = 1: every slice's loads carry the tile's activation scales of that chunk
+// (one 4-byte load per tile row).  SB = 4 (K a multiple of 4 chunks, 2-stage
+// ring): each scale-loading wavefront brings its 64 rows' scales of 4 chunks
+// at once (16 bytes per lane) into a 2-group scale buffer, once every 4 slices,
+// so a slice issues a quarter as many scale requests; the scales themselves,
+// and so every output bit, are the same.
+template <int MODE, int WM, int WN, int MI, int NI, int STAGES, int SB>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) {
   constexpr int NW = WM * WN, NT = 64 * NW;
   constexpr int BM = WM * MI * 16, BN = WN * NI * 16;
@@ -117,16 +123,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   constexpr int SA_W = BM / 64;                       // wavefronts that load activation scales
   static_assert(BM % 64 == 0 && SA_W <= NW, "64 scale rows per loading wavefront");
   constexpr int PER = A_CH + B_CH + 1;                // loads per thread per slice
+  constexpr bool BATCH = SB == 4;
+  static_assert(SB == 1 || (SB == 4 && STAGES == 2), "scale groups of 4 chunks need the 2-stage ring");
   static_assert(MODE != kGateUp8 || BN == 256, "a gate/up tile is one 1 x 128 tile of h");
   static_assert(MODE != kDown8 || (128 % (NI * 16) == 0), "a wavefront's columns in one weight block");
-  // LDS layout (bytes): STAGES x [A rows | B rows | sa[BM] | dummy scale rows],
-  // then sw[2][kFp8MaxKC], then red[BM][WN]
+  // LDS layout (bytes): STAGES x [A rows | B rows | sa[BM] | dummy scale rows]
+  // (SB = 4: STAGES x [A rows | B rows], then the scale groups sg[2][BM][4]),
+  // then sw[2][kFp8MaxKC], then red[BM][WN] (SB = 4: also the target of the
+  // slices' dropped scale loads, which write zeros there before the epilogue
+  // uses it)
   constexpr int SA_OFF = (BM + BN) * BK;
   constexpr int DUMMY_OFF = SA_OFF + BM * 4;
-  constexpr int STAGE = DUMMY_OFF + (NW - SA_W) * 256;
+  constexpr int STAGE = BATCH ? SA_OFF : DUMMY_OFF + (NW - SA_W) * 256;
   static_assert(STAGE % 16 == 0, "stage alignment");
-  constexpr int SW_OFF = STAGES * STAGE;
+  constexpr int SG_OFF = STAGES * STAGE;
+  constexpr int SW_OFF = SG_OFF + (BATCH ? 2 * BM * 16 : 0);
   constexpr int RED_OFF = SW_OFF + 2 * kFp8MaxKC * 4;
+  static_assert(!BATCH || BM * WN * 4 >= NW * 256, "dropped scale loads fit in red");
+  constexpr int SA_STRIDE = BATCH ? 4 : 1;            // floats per row of the slice's scales
   // down epilogue: each wavefront stages its (MI*16) x (NI*16) bf16 outputs in LDS
   // (rows padded to STG_PITCH bytes against bank conflicts) over the finished ring
   constexpr int STG_PITCH = NI * 16 * 2 + 16;
@@ -140,7 +154,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
   float* sw_lds = reinterpret_cast<float*>(lds + SW_OFF);
   float* red = reinterpret_cast<float*>(lds + RED_OFF);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wavefront index is uniform: kept in an SGPR, so are the load choices below)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, g = lane >> 4;
 
@@ -232,6 +247,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     if (gather && wave < SA_W && sa_row < rows) sa_src = p.perm[row0 + sa_row] / p.k;
   const int sa_off = sa_src * KC * 4;
   const int sa_dst = wave < SA_W ? SA_OFF + wave * 256 : DUMMY_OFF + (wave - SA_W) * 256;
+  const int sa_drop = (a_rows + 1) * KC * 4;           // SB = 4: past the scale descriptor (dropped)
   const __amdgpu_buffer_rsrc_t rsrc_a = rsrc_of(A, a_rows * lda);
   const __amdgpu_buffer_rsrc_t rsrc_w = rsrc_of(W, w_bytes);
   const __amdgpu_buffer_rsrc_t rsrc_s = rsrc_of(SA, a_rows * KC * 4);
@@ -248,11 +264,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                                 \
         __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
             rsrc_w, (lds_void_t*)(sb + BM * BK + (i * NW + wave) * 1024), 16, b_off[i], wk, 0, 0);   \
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_void_t*)(sb + sa_dst), 4, sa_off, kcv * 4, \
-                                             0, 0);                                                  \
+    if constexpr (!BATCH) {                                                                          \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_void_t*)(sb + sa_dst), 4, sa_off, kcv * 4, \
+                                               0, 0);                                                \
+    } else {                                                                                         \
+      /* group G = (kc + 3) / 4 of chunks [4G, 4G + 4): its quarter from wavefront */                 \
+      /* w = kc mod 4 (and 4 with 0), so slices 4G-3 .. 4G bring the whole group */                  \
+      const int grp = (kcv + 3) >> 2;                                                                \
+      if (wave < SA_W && (wave & 3) == (kcv & 3) && 4 * grp < KC)                                    \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                                    \
+            rsrc_s, (lds_void_t*)(lds + SG_OFF + (grp & 1) * BM * 16 + wave * 1024), 16, sa_off,     \
+            grp * 16, 0, 0);                                                                         \
+      else                                                                                           \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_void_t*)(lds + RED_OFF + wave * 256), 4, \
+                                                 sa_drop, 0, 0, 0);                                  \
+    }                                                                                                \
   }
 
   const int nk = KC;
+  // SB = 4: scale group 0 before the ring (the first slice's wait covers it)
+  if constexpr (BATCH)
+    if (wave < SA_W)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc_s, (lds_void_t*)(lds + SG_OFF + wave * 1024), 16, sa_off, 0,
+                                               0, 0);
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
     if (s < nk) MOE_ISSUE8(s, s);
@@ -295,7 +329,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
     }
     if (has_rows) {
       const uint8_t* base = lds + cur * STAGE;
-      const float* sa_st = reinterpret_cast<const float*>(base + SA_OFF);
+      // this slice's scale of each tile row (SB = 4: entry kt mod 4 of group kt / 4)
+      const float* sa_st = BATCH ? reinterpret_cast<const float*>(lds + SG_OFF) + ((kt >> 2) & 1) * BM * 4 + (kt & 3)
+                                 : reinterpret_cast<const float*>(base + SA_OFF);
       const float w0 = sw_lds[wsel * kFp8MaxKC + kt];
       const float w1 = sw_lds[kFp8MaxKC + kt];
       i32x8_t fb[NI];
@@ -305,7 +341,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
       // and scale reads are issued before this block's MFMAs, and the previous
       // block's chunk products are promoted (VALU) under this block's MFMAs
       const uint8_t* pa = base + arow0 * BK;   // this lane's A row in block 0; block mi is 16 mi rows further
-      const float* psa = sa_st + arow0;
+      const float* psa = sa_st + arow0 * SA_STRIDE;
       i32x8_t fa = frag(pa, c_lo, c_hi);
       float sa = psa[0];
       f32x4_t prev[NI];
@@ -316,7 +352,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_fp8_kernel(Fp8Params p) 
         float sa_n = 0.f;
         if (mi + 1 < MI) {
           fa_n = frag(pa + (mi + 1) * 16 * BK, c_lo, c_hi);
-          sa_n = psa[(mi + 1) * 16];
+          sa_n = psa[(mi + 1) * 16 * SA_STRIDE];
         }
         __builtin_amdgcn_sched_barrier(0);
         const float s0 = sa * w0, s1 = sa * w1;
@@ -478,8 +514,12 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.ntiles = hdr;
     const int64_t grid = grouped_grid(L.max1, kStripeFp8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
-                         dim3(kThreads8), 0, st, p);
+      if ((c->H / 128) % 4 == 0)   // K = H in whole groups of 4 chunks
+        hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, kWM8, kWN8, kMI8, kNI8, 2, 4>), dim3((unsigned)grid),
+                           dim3(kThreads8), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_fp8_kernel<kGateUp8, kWM8, kWN8, kMI8, kNI8, 2, 1>), dim3((unsigned)grid),
+                           dim3(kThreads8), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
@@ -495,8 +535,12 @@ moe_status launch_ffn_fp8(const moe_cfg* c, const fp8_t* x_perm, const float* x_
     p.ntiles = hdr + 1;
     const int64_t grid = grouped_grid(L.max2, kStripeFp8);
     if (grid > 0) {
-      hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, kWM8, kWN8, kMI8, kNI8, 2>), dim3((unsigned)grid),
-                         dim3(kThreads8), 0, st, p);
+      if ((c->I / 128) % 4 == 0)   // K = I (routed) and S * I (shared) in whole groups of 4 chunks
+        hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, kWM8, kWN8, kMI8, kNI8, 2, 4>), dim3((unsigned)grid),
+                           dim3(kThreads8), 0, st, p);
+      else
+        hipLaunchKernelGGL((gemm_fp8_kernel<kDown8, kWM8, kWN8, kMI8, kNI8, 2, 1>), dim3((unsigned)grid),
+                           dim3(kThreads8), 0, st, p);
       if ((s = launch_status()) != MOE_OK) return s;
     }
   }
