@@ -127,6 +127,10 @@ FFN8_CASES = [
     (1000, 1024, 64, 8, 3, 6, 2, 256),
     (200, 7168, 8, 2, 2, 2, 1, 256),
     (130, 8192, 4, 2, 1, 2, 1, 128),
+    # K in whole groups of 4 chunks (activation scales loaded 4 chunks at a time) in both GEMMs:
+    # one group (H = 512), the shared down GEMM over 2 experts' 8 chunks; 3 groups (H = 1536)
+    (300, 512, 16, 4, 2, 4, 2, 512),
+    (257, 1536, 8, 2, 2, 2, 1, 1024),
 ]
 
 
